@@ -1,0 +1,189 @@
+/*
+ * mla.h — C ABI of libmla.so: multi-head latent attention (MLA) decode over a
+ * compressed KV cache, and the literal wkv_b key/value reconstruction, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources for the operations (web pages, cited by title and section):
+ *   [KVR]  "KV Reconstruction" (DeepSeek-V3 study note): "How it works"
+ *          (up-projection equations, absorb identities, scale 1/sqrt(192)),
+ *          "Official code", "Watch-outs".
+ *   [ABS]  "DeepSeek-V3.2-Exp · Absorb key weights": the absorb equation,
+ *          "Explanation", and its MQA-decode code excerpt.
+ *   [KVL]  "DeepSeek-V3.2-Exp · Key–value latent": the mla-init, mla-kv,
+ *          linear (FP8 block scales) and rmsnorm code excerpts.
+ *   [VUP]  "Value up-projection" (DeepSeek-V3.2-Exp atlas): in/out shapes,
+ *          parameter table, "Explanation", prefill code excerpt.
+ *   [DS3]  "DeepSeek V3" (inference notes): "Multi-Head Latent Attention"
+ *          equations, "Decoupled RoPE" (cache size), inference data flow.
+ *
+ * Fixed dimensions (see [KVR] "How it works", [KVL] mla-init excerpt):
+ *   d_c = 512 latent features (kv_lora_rank), d_R = 64 rotary features,
+ *   d_h = 128 content ("nope") features per head = 128 value features.
+ * wkv_b is always the [n_h*256, 512] matrix stored [out, in] ([VUP]
+ * "Parameters"), viewed as [n_h][256][512]: rows 0..127 of each head are
+ * W^UK and rows 128..255 are W^UV ([KVR] "Official code", [ABS] excerpt).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to caller-owned memory,
+ *     row-major and densely packed unless a stride argument says otherwise.
+ *     The library never allocates, frees or synchronises.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the null stream). Inputs must stay valid until the work completes.
+ *   - mla_dtype selects the element type of the floating-point tensors of a
+ *     call: MLA_F32 (float) or MLA_BF16 (bfloat16 bits in uint16_t). All
+ *     sums accumulate in fp32; bf16 results are rounded to nearest-even.
+ *   - Arguments are checked on the host before anything is enqueued. A bad
+ *     argument returns MLA_ERR_INVALID_ARG and a dimension or layout this
+ *     build does not implement returns MLA_ERR_UNSUPPORTED; in both cases no
+ *     HIP call is made. A failed launch returns MLA_ERR_HIP. The detail of
+ *     the last failure on the calling thread is in mla_last_error().
+ *   - A call whose batch/row count is zero is a no-op returning MLA_OK.
+ *   - Pointers must be 16-byte aligned; element strides must keep every row
+ *     16-byte aligned (multiples of 8 bf16 or 4 f32 elements).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad index count  */
+  MLA_ERR_UNSUPPORTED = 2, /* dimension/stride/alignment not implemented    */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  MLA_ERR_HIP = 4          /* the HIP runtime reported an error at launch   */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_str(mla_status status);
+
+/* Detail message of the last non-OK status returned on this thread
+ * (static thread-local storage; "" if none). */
+const char* mla_last_error(void);
+
+/*
+ * One-time FP8 block dequantisation of a weight ([KVL] linear excerpt: one
+ * fp32 scale per 128x128 block of a 1-byte weight; [ABS] excerpt: wkv_b is
+ * dequantised once and reused for decoding).
+ *   w_fp8  [rows, cols] uint8, OCP E4M3 ("e4m3fn": bias 7, no infinities,
+ *          S.1111.111 is NaN, max 448).
+ *   scale  [ceil(rows/128), ceil(cols/128)] float32.
+ *   w_bf16 [rows, cols] out: bf16( f32( decode(w[i,j]) * scale[i/128, j/128] ) )
+ *          with the product rounded to fp32 and then to bf16, each to
+ *          nearest-even. NaN codes produce a NaN (payload unspecified).
+ * Requirements: cols % 16 == 0. rows == 0 or cols == 0 is a no-op.
+ */
+mla_status mla_dequant_fp8_block(const uint8_t* w_fp8, const float* scale,
+                                 int64_t rows, int64_t cols, uint16_t* w_bf16,
+                                 hipStream_t stream);
+
+/*
+ * Absorb W^UK into the content query ([ABS] equation and excerpt;
+ * [KVR] "How it works", first absorb identity):
+ *   q_lat[b,h,c] = sum_{d<128} q_nope[b,h,d] * wkv_b[h*256 + d, c]
+ *   q_nope [B, n_h, 128], wkv_b [n_h*256, 512], q_lat [B, n_h, 512] (out);
+ *   all of element type dt.
+ */
+mla_status mla_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat,
+                        int B, int n_h, mla_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of workspace mla_decode_latent_attn needs for these arguments
+ * (K = 0 for dense attention over all T positions; num_splits as passed to
+ * the decode call, 0 = automatic). Returns 0 when no workspace is needed,
+ * and (size_t)-1 for arguments the decode call would reject.
+ */
+size_t mla_decode_workspace_bytes(int B, int n_h, int T, int K, int num_splits,
+                                  mla_dtype dt);
+
+/* The split count the decode call uses for num_splits == 0 (>= 1), or -1
+ * for arguments the decode call would reject. */
+int mla_decode_num_splits(int B, int n_h, int T, int K);
+
+/*
+ * Latent attention of the absorbed decode path, one query token per
+ * sequence ([ABS] excerpt: scores against the latent and rotary caches,
+ * index mask, softmax, probability-weighted latent; [KVR] "How it works":
+ * rotary scores are added to the content scores; the scale is applied to
+ * their sum):
+ *   z[b,h,t]     = scale * ( sum_c q_lat[b,h,c] * latent[b,t,c]
+ *                          + sum_r q_pe[b,h,r]  * rope[b,t,r] ),  t < T
+ *   z[b,h,t]     = -inf for every h when topk_idx is given and t is not in
+ *                  topk_idx[b, 0..K-1]
+ *   p[b,h,:]     = softmax_t z[b,h,:]
+ *   out_lat[b,h,c] = sum_t p[b,h,t] * latent[b,t,c]
+ *   lse[b,h]     = log sum_t exp z[b,h,t]   (natural log; optional)
+ *
+ *   q_lat  [B, n_h, 512], q_pe [B, n_h, 64]            (dt)
+ *   latent element (b,t,c) at latent[b*lat_bstride + t*lat_rstride + c]
+ *   rope   element (b,t,r) at rope  [b*rope_bstride + t*rope_rstride + r]
+ *          (dt; strides in elements). Two layouts are typical: separate
+ *          latent [B_max,T_max,512] and rope [B_max,T_max,64] caches read as
+ *          [:B, :T], or one packed [B,T,576] cache with latent = p,
+ *          rope = p + 512 and both row strides 576.
+ *   topk_idx  NULL for dense attention over all T positions (K ignored), or
+ *          int32 [B, K] with 1 <= K <= T DISTINCT positions in [0, T) per
+ *          sequence, in any order. Index contents are NOT checked on the
+ *          device: out-of-range entries read outside the cache and
+ *          duplicates are counted twice; callers must guarantee the contract.
+ *   out_lat [B, n_h, 512] (dt, out), lse [B, n_h] float32 (out, or NULL).
+ *   num_splits  number of partitions of the attended positions (0 = let the
+ *          library choose; otherwise 1 <= num_splits <= ceil(rows/32), where
+ *          rows = T, or K with topk_idx). Results differ between split counts
+ *          only by floating-point rounding.
+ *   workspace  device memory of at least
+ *          mla_decode_workspace_bytes(B, n_h, T, K, num_splits, dt) bytes
+ *          (may be NULL when that is 0).
+ * Requirements: n_h >= 1, T >= 1; lat_rstride >= 512, rope_rstride >= 64,
+ *   row strides multiples of 8 (bf16) or 4 (f32) elements, batch strides
+ *   >= 0 (0 shares one cache among all sequences).
+ */
+mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe,
+                                  const void* latent, const void* rope,
+                                  int64_t lat_bstride, int64_t lat_rstride,
+                                  int64_t rope_bstride, int64_t rope_rstride,
+                                  int B, int n_h, int T,
+                                  const int32_t* topk_idx, int K, float scale,
+                                  int num_splits, void* out_lat, float* lse,
+                                  void* workspace, size_t ws_bytes,
+                                  mla_dtype dt, hipStream_t stream);
+
+/*
+ * W^UV after the probability-weighted sum ([KVR] "How it works", second
+ * absorb identity, and "Watch-outs": attend on the latent, then W^UV;
+ * [ABS] excerpt, last einsum; [VUP] "Explanation": value rows are 128..255
+ * of each head's 256):
+ *   out[b,h,d] = sum_c out_lat[b,h,c] * wkv_b[h*256 + 128 + d, c]
+ *   out_lat [B, n_h, 512], wkv_b [n_h*256, 512], out [B, n_h, 128] (dt).
+ */
+mla_status mla_out_up(const void* out_lat, const void* wkv_b, void* out,
+                      int B, int n_h, mla_dtype dt, hipStream_t stream);
+
+/*
+ * Literal ("naive") key/value reconstruction ([KVR] "How it works": k^C =
+ * W^UK c, v^C = W^UV c, key = [k^C ; k^R]; [VUP] prefill excerpt: wkv_b,
+ * view per head, split into k_nope and v, concatenate the broadcast k^R):
+ *   kv[n,h,e] = sum_c wkv_b[h*256 + e, c] * c[n,c],   e < 256
+ *   K[n,h,0:128]   = kv[n,h,0:128]
+ *   K[n,h,128:192] = k_rope[n,0:64]   (an exact copy, shared by all heads)
+ *   V[n,h,0:128]   = kv[n,h,128:256]
+ *   c [N, 512], k_rope [N, 64], wkv_b [n_h*256, 512],
+ *   K [N, n_h, 192] (out), V [N, n_h, 128] (out); all of element type dt.
+ */
+mla_status mla_kv_reconstruct(const void* c, const void* k_rope,
+                              const void* wkv_b, void* K, void* V, int64_t N,
+                              int n_h, mla_dtype dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */
