@@ -1,0 +1,234 @@
+"""Benchmark of the absorbed MLA decode step on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: mla_absorb_q -> mla_decode_latent_attn -> mla_out_up (plus, for the
+fp8 sparse workload, the weights are dequantised once before timing, as the
+method memoises them). Default workload: B=32, n_h=128, T=4096 cached
+positions, bf16, 1 query token per sequence.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by
+synchronisation, HIP events on the stream the kernels run on. Each step uses
+the next of R device replicas of the inputs (>= 1 GiB in total) so the
+256 MB Infinity Cache cannot serve the cache reads. Per-call durations come
+from events around each call inside the timed region.
+
+Prints ONE JSON line (metric/value/unit/..., roofline, cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "MLA absorbed decode: cached token·heads/s and % of HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
+                    help="decode workload (2: B=32 T=4096; 3: B=4 T=32768; 4: sparse fp8)")
+    ap.add_argument("--min-replica-bytes", type=float, default=1.1e9)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_work(B, n_h, rows, esz=2):
+    """Bytes that must move and flops that must happen (intermediates q_lat,
+    o_lat and split partials excluded). rows = attended positions/sequence."""
+    cache = B * rows * 576 * esz
+    w = n_h * 256 * 512 * esz
+    q = B * n_h * (128 + 64) * esz
+    out = B * n_h * 128 * esz
+    q_lat = B * n_h * 512 * esz
+    o_lat = B * n_h * 512 * esz
+    q_pe = B * n_h * 64 * esz
+    step_bytes = cache + w + q + out
+    attn_bytes = cache + q_lat + q_pe + o_lat
+    attn_flops = B * rows * n_h * (576 + 512) * 2
+    step_flops = attn_flops + 2 * B * n_h * 128 * 512 * 2
+    return dict(step_bytes=step_bytes, step_flops=step_flops, attn_bytes=attn_bytes,
+                attn_flops=attn_flops, cache_bytes=cache, w_bytes=w)
+
+
+def roofline_time_s(nbytes, flops):
+    return max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12))
+
+
+def traffic_record(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "head_latent_attention_mla_amd", "csrc", rec["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["bytes_per_launch"] if digest == rec["source_sha256_16"] else None
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle (as written, untuned) on the same workload, host cores."""
+    import numpy as np  # noqa: F401
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    cache = inp["cache"]
+    B = cache.shape[0]
+    nb = B  # whole batch: 10-30 s of CPU work on a 16-core host share
+    if cfg == 4:
+        w = inp["wkv_b_ref"]
+        topk = inp["topk_idx"][:nb]
+    else:
+        w = inp["wkv_b"]
+        topk = None
+    t0 = time.perf_counter()
+    oracle.decode_absorbed(inp["q_nope"][:nb], inp["q_pe"][:nb], cache[:nb, :, :512],
+                           cache[:nb, :, 512:], w, topk_idx=topk)
+    dt = time.perf_counter() - t0
+    n_h = inp["q_nope"].shape[1]
+    rows = topk.shape[1] if topk is not None else cache.shape[1]
+    return {"value": nb * rows * n_h / dt, "unit": "cached token·heads/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"one full decode step of {nb} sequences x {rows} positions x {n_h} heads, "
+                      f"fp64 C oracle, OpenMP over (sequence, head)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not "
+                          "supported (--gpus must be 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from head_latent_attention_mla_amd import binding as mla
+    from head_latent_attention_mla_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    B, n_h, T = cfg["B"], cfg["n_h"], cfg["T"]
+    inp = synth.config_inputs(args.config)
+    sparse = "topk_idx" in inp
+    rows = inp["topk_idx"].shape[1] if sparse else T
+
+    # device replicas (inputs resident in HBM before timing)
+    if args.config == 4:
+        w0 = mla.mla_dequant_fp8_block(inp["wkv_b_fp8"].to(dev), inp["wkv_b_scale"].to(dev))
+        torch.cuda.synchronize()
+        inp["wkv_b_ref"] = w0.cpu()
+    else:
+        w0 = inp["wkv_b"].to(dev)
+    base = dict(cache=inp["cache"].to(dev), q_nope=inp["q_nope"].to(dev),
+                q_pe=inp["q_pe"].to(dev), w=w0,
+                topk=inp["topk_idx"].to(dev) if sparse else None)
+    per_rep = (base["cache"].numel() * 2 + w0.numel() * 2 if not sparse
+               else B * rows * 576 * 2 + w0.numel() * 2)
+    R = max(2, int(-(-args.min_replica_bytes // per_rep)))
+    if sparse:
+        R = max(R, 2)
+    reps = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                     for _ in range(R - 1)]
+    q_lat = torch.empty((B, n_h, 512), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, n_h, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, n_h, 128), dtype=torch.bfloat16, device=dev)
+    K = rows if sparse else 0
+    ws_bytes = mla.mla_decode_workspace_bytes(B, n_h, T, K, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    splits = mla.mla_decode_num_splits(B, n_h, T, K)
+
+    def step(r, ev=None):
+        x = reps[r % R]
+        if ev is not None:
+            ev[0].record()
+        mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
+        if ev is not None:
+            ev[1].record()
+        mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
+                                   x["cache"][..., 512:], topk_idx=x["topk"], out_lat=o_lat,
+                                   workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        mla.mla_out_up(o_lat, x["w"], out)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, bracketed by synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    absorb_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    outup_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    work = algorithmic_work(B, n_h, rows)
+    value = B * rows * n_h / (ms_step * 1e-3)
+    t_roof_step = roofline_time_s(work["step_bytes"], work["step_flops"])
+    # dominant kernel: the latent attention call (split kernel + merge kernel)
+    attn_gbs = work["attn_bytes"] / (decode_ms * 1e-3) / 1e9
+    traffic = traffic_record(f"decode_config{args.config}")
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "cached token·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no datasets or trained weights)",
+        "config": {"workload": cfg["name"], "B": B, "n_h": n_h, "T": T,
+                   "attended_positions": rows, "query_tokens": 1,
+                   "fp8_weights": bool(cfg.get("fp8_weights", False)),
+                   "decode_splits": splits, "input_replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_latent_attn (split + merge launches)",
+                     "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": work["attn_bytes"],
+                     "avg_launch_us": decode_ms * 1e3},
+        "step": {"roofline_us": t_roof_step * 1e6, "frac_of_roofline": t_roof_step / (ms_step * 1e-3),
+                 "bytes": work["step_bytes"], "flops": work["step_flops"],
+                 "GB_s": work["step_bytes"] / (ms_step * 1e-3) / 1e9,
+                 "TFLOP_s": work["step_flops"] / (ms_step * 1e-3) / 1e12,
+                 "absorb_us": absorb_ms * 1e3, "decode_us": decode_ms * 1e3,
+                 "out_up_us": outup_ms * 1e3},
+        "published_baseline": "none: the source pages print no throughput figures",
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config, inp)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+"""Python binding of libmla.so (the C ABI in include/mla.h).
+
+Argument marshalling only: every function checks torch tensor metadata,
+allocates outputs the caller did not pass (torch device memory), and calls
+the C entry point of the same name on the current HIP stream. All compute
+happens in the library's HIP kernels; there is no fallback of any kind, and
+a missing library raises MLAError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+SCALE = 192 ** -0.5  # 1 / sqrt(d_h + d_h^R)
+
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
+           3: "MLA_ERR_WORKSPACE", 4: "MLA_ERR_HIP"}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} {detail}".strip())
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libmla.so (raises MLAError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MLAError("load", -1, f"{LIB_PATH} is missing; build it with "
+                           "`python -m head_latent_attention_mla_amd._build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, L, F, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                         ctypes.c_size_t)
+        lib.mla_status_str.argtypes = [I]
+        lib.mla_status_str.restype = ctypes.c_char_p
+        lib.mla_last_error.argtypes = []
+        lib.mla_last_error.restype = ctypes.c_char_p
+        lib.mla_dequant_fp8_block.argtypes = [P, P, L, L, P, P]
+        lib.mla_absorb_q.argtypes = [P, P, P, I, I, I, P]
+        lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        lib.mla_decode_workspace_bytes.restype = Z
+        lib.mla_decode_num_splits.argtypes = [I, I, I, I]
+        lib.mla_decode_num_splits.restype = I
+        lib.mla_decode_latent_attn.argtypes = [P, P, P, P, L, L, L, L, I, I, I, P, I, F, I,
+                                               P, P, P, Z, I, P]
+        lib.mla_out_up.argtypes = [P, P, P, I, I, I, P]
+        lib.mla_kv_reconstruct.argtypes = [P, P, P, P, P, L, I, I, P]
+        for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
+                     "mla_out_up", "mla_kv_reconstruct"):
+            getattr(lib, name).restype = I
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MLAError(fn, status, library().mla_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            _require(t.is_cuda, "tensors must be on the GPU")
+
+
+def mla_dequant_fp8_block(w_fp8: torch.Tensor, scale: torch.Tensor, out: torch.Tensor = None,
+                          stream=None) -> torch.Tensor:
+    """bf16 [rows, cols] = e4m3 codes (uint8) x fp32 scale per 128x128 block."""
+    _dev(w_fp8, scale, out)
+    _require(w_fp8.dtype == torch.uint8 and w_fp8.dim() == 2 and w_fp8.is_contiguous(),
+             "w_fp8 must be a contiguous 2-D uint8 tensor")
+    rows, cols = w_fp8.shape
+    _require(scale.dtype == torch.float32 and scale.is_contiguous() and
+             tuple(scale.shape) == ((rows + 127) // 128, (cols + 127) // 128),
+             "scale must be contiguous float32 [ceil(rows/128), ceil(cols/128)]")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=w_fp8.device)
+    _require(out.dtype == torch.bfloat16 and out.is_contiguous() and out.shape == w_fp8.shape,
+             "out must be contiguous bf16 of the same shape")
+    _check("mla_dequant_fp8_block", library().mla_dequant_fp8_block(
+        _ptr(w_fp8), _ptr(scale), rows, cols, _ptr(out), _stream(stream)))
+    return out
+
+
+def mla_absorb_q(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_lat: torch.Tensor = None,
+                 stream=None) -> torch.Tensor:
+    """q_lat [B, n_h, 512] = q_nope [B, n_h, 128] absorbed with W^UK of wkv_b."""
+    _dev(q_nope, wkv_b, q_lat)
+    B, n_h, d = q_nope.shape
+    _require(d == 128 and q_nope.is_contiguous(), "q_nope must be contiguous [B, n_h, 128]")
+    _require(wkv_b.dtype == q_nope.dtype and wkv_b.is_contiguous() and
+             tuple(wkv_b.shape) == (n_h * 256, 512), "wkv_b must be contiguous [n_h*256, 512]")
+    if q_lat is None:
+        q_lat = torch.empty((B, n_h, 512), dtype=q_nope.dtype, device=q_nope.device)
+    _require(q_lat.dtype == q_nope.dtype and q_lat.is_contiguous() and
+             tuple(q_lat.shape) == (B, n_h, 512), "q_lat must be contiguous [B, n_h, 512]")
+    _check("mla_absorb_q", library().mla_absorb_q(
+        _ptr(q_nope), _ptr(wkv_b), _ptr(q_lat), B, n_h, _dtype_code(q_nope), _stream(stream)))
+    return q_lat
+
+
+def mla_decode_workspace_bytes(B: int, n_h: int, T: int, K: int = 0, num_splits: int = 0,
+                               dtype=torch.bfloat16) -> int:
+    code = MLA_BF16 if dtype == torch.bfloat16 else MLA_F32
+    v = library().mla_decode_workspace_bytes(B, n_h, T, K, num_splits, code)
+    if v == ctypes.c_size_t(-1).value:
+        raise MLAError("mla_decode_workspace_bytes", 1, "arguments rejected")
+    return v
+
+
+def mla_decode_num_splits(B: int, n_h: int, T: int, K: int = 0) -> int:
+    v = library().mla_decode_num_splits(B, n_h, T, K)
+    if v < 0:
+        raise MLAError("mla_decode_num_splits", 1, "arguments rejected")
+    return v
+
+
+def _cache_strides(t: torch.Tensor, width: int, name: str):
+    _require(t.dim() == 3 and t.stride(2) == 1 and t.shape[2] == width,
+             f"{name} must be [B, T_alloc, {width}] with unit stride in the last dim")
+    return t.stride(0), t.stride(1)
+
+
+def mla_decode_latent_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, latent: torch.Tensor,
+                           rope: torch.Tensor, T: int = None, topk_idx: torch.Tensor = None,
+                           scale: float = SCALE, num_splits: int = 0,
+                           out_lat: torch.Tensor = None, lse: torch.Tensor = None,
+                           workspace: torch.Tensor = None, want_lse: bool = False,
+                           stream=None):
+    """Latent attention of the absorbed decode step.
+
+    latent [B, T_alloc, 512] and rope [B, T_alloc, 64] may be views of one
+    packed [B, T_alloc, 576] cache (cache[..., :512], cache[..., 512:]).
+    Returns out_lat [B, n_h, 512] (and lse [B, n_h] fp32 if requested).
+    """
+    _dev(q_lat, q_pe, latent, rope, topk_idx, out_lat, lse, workspace)
+    B, n_h, d = q_lat.shape
+    _require(d == 512 and q_lat.is_contiguous(), "q_lat must be contiguous [B, n_h, 512]")
+    _require(q_pe.dtype == q_lat.dtype and q_pe.is_contiguous() and
+             tuple(q_pe.shape) == (B, n_h, 64), "q_pe must be contiguous [B, n_h, 64]")
+    _require(latent.dtype == q_lat.dtype and rope.dtype == q_lat.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    _require(latent.shape[0] >= B and rope.shape[0] >= B, "cache batch too small")
+    if T is None:
+        T = latent.shape[1]
+    _require(T <= latent.shape[1] and T <= rope.shape[1], "T exceeds the cache length")
+    K = 0
+    if topk_idx is not None:
+        _require(topk_idx.dtype == torch.int32 and topk_idx.is_contiguous() and
+                 topk_idx.dim() == 2 and topk_idx.shape[0] == B,
+                 "topk_idx must be contiguous int32 [B, K]")
+        K = topk_idx.shape[1]
+    if out_lat is None:
+        out_lat = torch.empty((B, n_h, 512), dtype=q_lat.dtype, device=q_lat.device)
+    _require(out_lat.dtype == q_lat.dtype and out_lat.is_contiguous() and
+             tuple(out_lat.shape) == (B, n_h, 512), "out_lat must be contiguous [B, n_h, 512]")
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_h), dtype=torch.float32, device=q_lat.device)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and
+                 tuple(lse.shape) == (B, n_h), "lse must be contiguous float32 [B, n_h]")
+    need = mla_decode_workspace_bytes(B, n_h, T, K, num_splits, q_lat.dtype) if B > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_latent_attn", library().mla_decode_latent_attn(
+        _ptr(q_lat), _ptr(q_pe), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B, n_h, T,
+        _ptr(topk_idx), K, float(scale), num_splits, _ptr(out_lat), _ptr(lse),
+        _ptr(workspace), ws_bytes, _dtype_code(q_lat), _stream(stream)))
+    return (out_lat, lse) if (want_lse or lse is not None) else out_lat
+
+
+def mla_out_up(out_lat: torch.Tensor, wkv_b: torch.Tensor, out: torch.Tensor = None,
+               stream=None) -> torch.Tensor:
+    """out [B, n_h, 128] = W^UV of wkv_b applied to out_lat [B, n_h, 512]."""
+    _dev(out_lat, wkv_b, out)
+    B, n_h, d = out_lat.shape
+    _require(d == 512 and out_lat.is_contiguous(), "out_lat must be contiguous [B, n_h, 512]")
+    _require(wkv_b.dtype == out_lat.dtype and wkv_b.is_contiguous() and
+             tuple(wkv_b.shape) == (n_h * 256, 512), "wkv_b must be contiguous [n_h*256, 512]")
+    if out is None:
+        out = torch.empty((B, n_h, 128), dtype=out_lat.dtype, device=out_lat.device)
+    _require(out.dtype == out_lat.dtype and out.is_contiguous() and
+             tuple(out.shape) == (B, n_h, 128), "out must be contiguous [B, n_h, 128]")
+    _check("mla_out_up", library().mla_out_up(
+        _ptr(out_lat), _ptr(wkv_b), _ptr(out), B, n_h, _dtype_code(out_lat), _stream(stream)))
+    return out
+
+
+def mla_kv_reconstruct(c: torch.Tensor, k_rope: torch.Tensor, wkv_b: torch.Tensor,
+                       K: torch.Tensor = None, V: torch.Tensor = None, stream=None):
+    """(K [N, n_h, 192], V [N, n_h, 128]) from c [N, 512], k_rope [N, 64]."""
+    _dev(c, k_rope, wkv_b, K, V)
+    N, d = c.shape
+    _require(d == 512 and c.is_contiguous(), "c must be contiguous [N, 512]")
+    _require(k_rope.dtype == c.dtype and k_rope.is_contiguous() and
+             tuple(k_rope.shape) == (N, 64), "k_rope must be contiguous [N, 64]")
+    _require(wkv_b.dtype == c.dtype and wkv_b.is_contiguous() and wkv_b.dim() == 2 and
+             wkv_b.shape[1] == 512 and wkv_b.shape[0] % 256 == 0,
+             "wkv_b must be contiguous [n_h*256, 512]")
+    n_h = wkv_b.shape[0] // 256
+    if K is None:
+        K = torch.empty((N, n_h, 192), dtype=c.dtype, device=c.device)
+    if V is None:
+        V = torch.empty((N, n_h, 128), dtype=c.dtype, device=c.device)
+    _require(K.dtype == c.dtype and K.is_contiguous() and tuple(K.shape) == (N, n_h, 192),
+             "K must be contiguous [N, n_h, 192]")
+    _require(V.dtype == c.dtype and V.is_contiguous() and tuple(V.shape) == (N, n_h, 128),
+             "V must be contiguous [N, n_h, 128]")
+    _check("mla_kv_reconstruct", library().mla_kv_reconstruct(
+        _ptr(c), _ptr(k_rope), _ptr(wkv_b), _ptr(K), _ptr(V), N, n_h, _dtype_code(c),
+        _stream(stream)))
+    return K, V

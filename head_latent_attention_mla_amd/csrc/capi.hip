@@ -1,0 +1,247 @@
+// capi.hip — the C ABI of libmla (declared in include/mla.h): host-side
+// argument checks, split planning for the decode call, and kernel dispatch.
+// Every check happens before the first HIP call; the library never
+// allocates, frees or synchronises.
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+
+#include "mla.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace mla;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(mla_dtype dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+// Split plan of the decode call: rows are cut into 32-row tiles, splits get
+// equal tile counts. Automatic choice: aim at one 4-wave workgroup per
+// compute unit (256 on MI355X) without making any split empty.
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMaxSplits = 1024;
+// The top-k kernel stages one split's indices in LDS: at most 1024 rows.
+constexpr int kMaxSparseTilesPerSplit = 1024 / 32;
+
+struct SplitPlan {
+  int num_splits;
+  int tiles_per_split;
+};
+
+// requested == 0: automatic. Returns false for a split count outside
+// [minimum, tiles] (the minimum is 1 dense, ceil(tiles/32) with top-k).
+bool plan_splits(int B, int n_h, int rows, bool sparse, int requested, SplitPlan* out) {
+  const int ntiles = (rows + 31) / 32;
+  const int min_s = sparse ? (ntiles + kMaxSparseTilesPerSplit - 1) / kMaxSparseTilesPerSplit : 1;
+  int s = requested;
+  if (s == 0) {
+    const long base = static_cast<long>(B) * ((n_h + 127) / 128);
+    long want = (kTargetWorkgroups + base - 1) / base;
+    if (want < 1) want = 1;
+    s = static_cast<int>(want < ntiles ? want : ntiles);
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < min_s) s = min_s;
+  }
+  if (s < min_s || s > ntiles) return false;
+  const int tps = (ntiles + s - 1) / s;
+  out->tiles_per_split = tps;
+  out->num_splits = (ntiles + tps - 1) / tps;  // no empty split
+  return true;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t ws_bytes_for(int B, int n_h, const SplitPlan& sp, mla_dtype dt) {
+  if (sp.num_splits == 1) return 0;
+  const size_t bh = static_cast<size_t>(B) * n_h * sp.num_splits;
+  const size_t esz = dt == MLA_BF16 ? 2 : 4;
+  return align256(bh * D_C * esz) + align256(bh * sizeof(float));
+}
+
+// decode argument checks shared by the size query and the call
+mla_status check_decode_dims(int B, int n_h, int T, int K, bool sparse, int* rows) {
+  if (B < 0) return fail(MLA_ERR_INVALID_ARG, "B=%d < 0", B);
+  if (n_h < 1) return fail(MLA_ERR_INVALID_ARG, "n_h=%d < 1", n_h);
+  if (T < 1) return fail(MLA_ERR_INVALID_ARG, "T=%d < 1", T);
+  if (sparse && (K < 1 || K > T))
+    return fail(MLA_ERR_INVALID_ARG, "top-k count K=%d outside [1, T=%d]", K, T);
+  *rows = sparse ? K : T;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status st) {
+  switch (st) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error; }
+
+mla_status mla_dequant_fp8_block(const uint8_t* w_fp8, const float* scale, int64_t rows,
+                                 int64_t cols, uint16_t* w_bf16, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(MLA_ERR_INVALID_ARG, "negative size %lld x %lld",
+                                        (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return MLA_OK;
+  if (!w_fp8 || !scale || !w_bf16) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (cols % 16) return fail(MLA_ERR_UNSUPPORTED, "cols=%lld not a multiple of 16", (long long)cols);
+  if (!aligned16(w_fp8) || !aligned16(w_bf16) || (reinterpret_cast<uintptr_t>(scale) & 3))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  return from_hip(launch_dequant_fp8_block(w_fp8, scale, rows, cols, w_bf16, stream),
+                  "dequant launch");
+}
+
+mla_status mla_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, int B, int n_h,
+                        mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 0 || n_h < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d n_h=%d", B, n_h);
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !wkv_b || !q_lat) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_lat))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  return from_hip(launch_absorb_q(q_nope, wkv_b, q_lat, B, n_h, dt == MLA_BF16, stream),
+                  "absorb launch");
+}
+
+int mla_decode_num_splits(int B, int n_h, int T, int K) {
+  int rows;
+  if (check_decode_dims(B, n_h, T, K, K > 0, &rows) != MLA_OK) return -1;
+  SplitPlan sp;
+  if (!plan_splits(B > 0 ? B : 1, n_h, rows, K > 0, 0, &sp)) return -1;
+  return sp.num_splits;
+}
+
+size_t mla_decode_workspace_bytes(int B, int n_h, int T, int K, int num_splits, mla_dtype dt) {
+  int rows;
+  if (!dtype_ok(dt) || num_splits < 0) return static_cast<size_t>(-1);
+  if (check_decode_dims(B, n_h, T, K, K > 0, &rows) != MLA_OK) return static_cast<size_t>(-1);
+  if (B == 0) return 0;
+  SplitPlan sp;
+  if (!plan_splits(B, n_h, rows, K > 0, num_splits, &sp)) return static_cast<size_t>(-1);
+  return ws_bytes_for(B, n_h, sp, dt);
+}
+
+mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const void* latent,
+                                  const void* rope, int64_t lat_bstride, int64_t lat_rstride,
+                                  int64_t rope_bstride, int64_t rope_rstride, int B, int n_h,
+                                  int T, const int32_t* topk_idx, int K, float scale,
+                                  int num_splits, void* out_lat, float* lse, void* workspace,
+                                  size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  const bool sparse = topk_idx != nullptr;
+  int rows;
+  mla_status st = check_decode_dims(B, n_h, T, K, sparse, &rows);
+  if (st != MLA_OK) return st;
+  if (B == 0) return MLA_OK;
+  if (B > 65535 || n_h > 65535) return fail(MLA_ERR_UNSUPPORTED, "B or n_h above 65535");
+  if (!q_lat || !q_pe || !latent || !rope || !out_lat)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (num_splits < 0) return fail(MLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
+  const int64_t ealign = dt == MLA_BF16 ? 8 : 4;
+  if (lat_rstride < D_C || rope_rstride < D_R)
+    return fail(MLA_ERR_INVALID_ARG, "row strides %lld/%lld below 512/64", (long long)lat_rstride,
+                (long long)rope_rstride);
+  if (lat_bstride < 0 || rope_bstride < 0)
+    return fail(MLA_ERR_INVALID_ARG, "negative batch stride");
+  if (lat_rstride % ealign || rope_rstride % ealign || lat_bstride % ealign ||
+      rope_bstride % ealign)
+    return fail(MLA_ERR_UNSUPPORTED, "strides must be multiples of %lld elements",
+                (long long)ealign);
+  if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(latent) || !aligned16(rope) ||
+      !aligned16(out_lat) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3)))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale is not finite");
+  SplitPlan sp;
+  if (!plan_splits(B, n_h, rows, sparse, num_splits, &sp))
+    return fail(MLA_ERR_INVALID_ARG, "num_splits=%d outside [%d, %d]", num_splits,
+                sparse ? ((rows + 31) / 32 + kMaxSparseTilesPerSplit - 1) / kMaxSparseTilesPerSplit
+                       : 1,
+                (rows + 31) / 32);
+  const size_t need = ws_bytes_for(B, n_h, sp, dt);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? ws_bytes : static_cast<size_t>(0));
+  if (need > 0 && !aligned16(workspace)) return fail(MLA_ERR_UNSUPPORTED, "misaligned workspace");
+
+  DecodeParams p{};
+  p.q_lat = q_lat;
+  p.q_pe = q_pe;
+  p.latent = latent;
+  p.rope = rope;
+  p.lat_bs = lat_bstride;
+  p.lat_rs = lat_rstride;
+  p.rope_bs = rope_bstride;
+  p.rope_rs = rope_rstride;
+  p.B = B;
+  p.n_h = n_h;
+  p.T = T;
+  p.idx = topk_idx;
+  p.K = sparse ? K : 0;
+  p.rows = rows;
+  p.num_splits = sp.num_splits;
+  p.tiles_per_split = sp.tiles_per_split;
+  p.scale = scale;
+  p.out_lat = out_lat;
+  p.lse = lse;
+  if (need > 0) {
+    const size_t bh = static_cast<size_t>(B) * n_h * sp.num_splits;
+    const size_t esz = dt == MLA_BF16 ? 2 : 4;
+    p.ws_o = workspace;
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(bh * D_C * esz));
+  }
+  return from_hip(launch_decode(p, dt == MLA_BF16, stream), "decode launch");
+}
+
+mla_status mla_out_up(const void* out_lat, const void* wkv_b, void* out, int B, int n_h,
+                      mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 0 || n_h < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d n_h=%d", B, n_h);
+  if (B == 0) return MLA_OK;
+  if (!out_lat || !wkv_b || !out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(out_lat) || !aligned16(wkv_b) || !aligned16(out))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  return from_hip(launch_out_up(out_lat, wkv_b, out, B, n_h, dt == MLA_BF16, stream),
+                  "out_up launch");
+}
+
+mla_status mla_kv_reconstruct(const void* c, const void* k_rope, const void* wkv_b, void* K,
+                              void* V, int64_t N, int n_h, mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (N < 0 || n_h < 1) return fail(MLA_ERR_INVALID_ARG, "N=%lld n_h=%d", (long long)N, n_h);
+  if (N == 0) return MLA_OK;
+  if (!c || !k_rope || !wkv_b || !K || !V) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(c) || !aligned16(k_rope) || !aligned16(wkv_b) || !aligned16(K) || !aligned16(V))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  if (N * n_h >= (static_cast<int64_t>(1) << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "N * n_h too large for one launch");
+  return from_hip(launch_kv_reconstruct(c, k_rope, wkv_b, K, V, N, n_h, dt == MLA_BF16, stream),
+                  "kv_reconstruct launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,543 @@
+// decode.hip — latent attention of the absorbed MLA decode path.
+//
+// Operation ("DeepSeek-V3.2-Exp · Absorb key weights", decode excerpt;
+// "KV Reconstruction", How it works):
+//   z[b,h,t] = scale * (q_lat[b,h,:] . latent[b,t,:] + q_pe[b,h,:] . rope[b,t,:])
+//   z = -inf at positions outside the top-k set (one set per sequence, shared
+//   by all heads), p = softmax_t z, out_lat[b,h,:] = sum_t p[b,h,t] latent[b,t,:]
+//
+// bf16 kernel (the hot path). One workgroup of 8 waves (2 per SIMD) per
+// (sequence, group of 128 heads, split of the attended rows). The workgroup
+// streams its rows in 32-row tiles (latent 512 + rotary 64 features) from HBM
+// into LDS with buffer_load ... lds (double-buffered: the next tile is in
+// flight while the current one is consumed), so each cached byte is read
+// from HBM once and shared by all 128 heads. LDS read bandwidth, not MFMA,
+// is the scarce resource on gfx950, so the work is split to maximise reuse
+// of every LDS read:
+//   scores   wave (hq, kh) computes the partial S^T[32 rows x 32 heads]
+//            of head quarter hq over feature half kh (18 k-steps of
+//            v_mfma_f32_32x32x16_bf16; A = cache rows via ds_read_b128,
+//            B = its queries, held in registers). The two halves meet in LDS.
+//   softmax  the kh = 1 wave of each pair owns the online softmax of its 32
+//            heads: each lane holds one head and 16 rows, so a tile max is 15
+//            in-lane maxima plus one cross-half exchange; the running max is
+//            raised lazily (only when a row beats it by 2^8), keeping the
+//            accumulator rescale off the common path. It publishes P (bf16,
+//            already in MFMA operand layout) and any rescale factors.
+//   mix      wave w owns latent features 64w..64w+63 of all 128 heads:
+//            O^T[64 x 128] += C^T[64 x 32 rows] . P^T[32 rows x 128 heads],
+//            16 MFMAs whose A operand (read with ds_read_b64_tr_b16, the
+//            gfx950 transposing LDS load) is reused across 4 head tiles.
+// Row and feature permutations (pi, tau) make each lane's score
+// accumulators 16 consecutive rows (exactly the P^T operand layout) and its
+// output accumulators 16 consecutive latent features (32-byte stores). LDS
+// tiles are XOR-swizzled per row (swz_lat / swz_rope) so the 16-byte score
+// reads and the transposing reads hit distinct banks.
+//
+// Splits: with S > 1 each split writes its normalised partial output (bf16)
+// and log-sum-exp to the workspace and a merge kernel combines them:
+//   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * out_s.
+//
+// fp32 kernel: a plain per-(sequence, head, split) VALU kernel used for the
+// float32 interface (a correctness path, not a performance path).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+constexpr int TILE = 32;                          // rows per tile
+constexpr int NWAVES = 8;                         // waves per workgroup
+constexpr int LAT_BYTES = TILE * D_C * 2;         // 32 KiB latent region
+constexpr int ROPE_BYTES = TILE * D_R * 2;        // 4 KiB rotary region
+constexpr int BUF_BYTES = LAT_BYTES + ROPE_BYTES; // one staged tile
+constexpr int MAX_SPARSE_ROWS = 1024;             // staged top-k indices per split
+constexpr int QK_STEPS = D_QK / 16 / 2;           // 18 k-steps per feature half
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// LDS tile layout: latent rows of 64 16-byte chunks, rotary rows of 8, with
+// the chunk index XOR-swizzled per row (inside aligned groups of 16 and 8
+// chunks). swz_lat is injective on the 16 rows a 16-byte score read serves
+// together ({0..3,16..19,4..7,20..23} and its +8 shift) and gives the 4
+// consecutive rows of a transposing read distinct bank quarters; swz_rope
+// does the same for 128-byte rotary rows (row parity supplies the 4th bit).
+__device__ __forceinline__ int swz_lat(int r) {
+  return ((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+}
+__device__ __forceinline__ int swz_rope(int r) {
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+}
+// Score A-operand row i reads tile row pi(i): accumulator r of lane half g is
+// then tile row 16g + r.
+__device__ __forceinline__ int pi_row(int i) {
+  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+// Mix A-operand rows come in blocks of 4 latent features; block beta holds
+// features 4*tau(beta)..+3 of a 32-feature tile, so accumulator r of lane
+// half g is feature 16g + r.
+__device__ __forceinline__ int tau_blk(int beta) { return 4 * (beta & 1) + (beta >> 1); }
+
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Raw buffer resource (base, no stride, 2^31-1 bytes, 32-bit format) in SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));
+  r[2] = 0x7FFFFFFF;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane i's 16 bytes at (rsrc base + soff + voff) land at LDS byte
+// lds_dst + 16*i. Issued from inline assembly so the compiler does not
+// serialise consecutive LDS-DMA loads; it has no register outputs, and the
+// caller waits with an explicit s_waitcnt vmcnt before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
+  const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lo));
+  const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(hi));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Stage rows [row0, row0+32) of this split into the LDS tile at byte address
+// `dst` (rows at or beyond row_end re-read row row_end-1; their
+// probabilities are zero). Latent: 4 instructions per wave, each one tile
+// row of 64 chunks (the row's global offset is a scalar). Rotary: waves 0..3
+// load 8 rows x 8 chunks each.
+template <bool SPARSE>
+__device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t lat_rb,
+                                           uint32_t rope_rb, const int* idx_lds, int row0,
+                                           int row_end, int row_begin, uint32_t dst, int wave,
+                                           int lane) {
+  const int valid = row_end - row0;
+#pragma unroll
+  for (int k = 0; k < TILE / NWAVES; k++) {
+    const int R = NWAVES * k + wave;  // wave-uniform tile row
+    const int Rc = R < valid ? R : valid - 1;
+    uint32_t grow;
+    if (SPARSE)
+      grow = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(idx_lds[row0 - row_begin + Rc]));
+    else
+      grow = static_cast<uint32_t>(row0 + Rc);
+    dma16(lat_d, dst + R * 1024, static_cast<uint32_t>((lane ^ swz_lat(R)) * 16),
+          __builtin_amdgcn_readfirstlane(grow * lat_rb));
+  }
+  if (wave < 4) {
+    const int R = 8 * wave + (lane >> 3);
+    const int Rc = R < valid ? R : valid - 1;
+    const uint32_t c = static_cast<uint32_t>((lane & 7) ^ swz_rope(R));
+    uint32_t voff, soff;
+    if (SPARSE) {
+      voff = static_cast<uint32_t>(idx_lds[row0 - row_begin + Rc]) * rope_rb + c * 16;
+      soff = 0;
+    } else {
+      voff = static_cast<uint32_t>(Rc) * rope_rb + c * 16;
+      soff = static_cast<uint32_t>(row0) * rope_rb;
+    }
+    dma16(rope_d, dst + LAT_BYTES + wave * 1024, voff, __builtin_amdgcn_readfirstlane(soff));
+  }
+}
+
+template <bool SPARSE>
+__global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char tiles[2 * BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // kh=0 partial scores
+  __shared__ __attribute__((aligned(16))) u32x4 pb[4 * 2 * 64];   // P operands [hq][kk][lane]
+  __shared__ float fac[128];                                       // rescale factor per head
+  __shared__ int flag[4];                                          // head quarter rescaled
+  __shared__ float linv[128];                                      // 1 / sum per head
+  __shared__ int idx_lds[SPARSE ? MAX_SPARSE_ROWS : 1];
+
+  const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int hq = wave & 3, kh = wave >> 2;  // score role: head quarter, feature half
+  const int head = hg * 128 + hq * 32 + n;  // score-role head of this lane
+  const int headc = min(head, p.n_h - 1);   // clamped for loads
+
+  const int row_begin = s * p.tiles_per_split * TILE;
+  const int row_end = min(p.rows, row_begin + p.tiles_per_split * TILE);
+  const int ntiles = (row_end - row_begin + TILE - 1) / TILE;
+
+  const i32x4 lat_d =
+      make_rsrc(static_cast<const uint16_t*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs);
+  const i32x4 rope_d =
+      make_rsrc(static_cast<const uint16_t*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs);
+  const uint32_t lat_rb = static_cast<uint32_t>(p.lat_rs * 2);  // row strides in bytes
+  const uint32_t rope_rb = static_cast<uint32_t>(p.rope_rs * 2);
+  const uint32_t tiles_addr = __builtin_amdgcn_readfirstlane(lds_addr(tiles));
+
+  if (SPARSE) {
+    const int* src = p.idx + static_cast<int64_t>(b) * p.K + row_begin;
+    for (int i = threadIdx.x; i < row_end - row_begin; i += NWAVES * 64) idx_lds[i] = src[i];
+    __syncthreads();
+  }
+  issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin, row_end, row_begin,
+                     tiles_addr, wave, lane);
+
+  // queries of the score role as MFMA B operands: k-step ks = 18kh + j covers
+  // features 16ks .. 16ks+15 of [q_lat ; q_pe], lane half g the 8 at 16ks + 8g
+  bf16x8 q[QK_STEPS];
+  {
+    const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
+    const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R;
+#pragma unroll
+    for (int j = 0; j < QK_STEPS; j++) {
+      const int f = 16 * (QK_STEPS * kh + j) + 8 * g;
+      q[j] = as_bf16x8(f < D_C ? ld16(ql + f) : ld16(qp + (f - D_C)));
+    }
+  }
+
+  // score-read offsets: chunk 2ks+g of tile row pi(n); the swizzle only
+  // touches the low chunk bits
+  const int srow = pi_row(n);
+  const int s_lat = srow * 1024;
+  const int s_lat_x = g ^ swz_lat(srow);
+  const int s_rope = LAT_BYTES + srow * 128;
+  const int s_rope_x = g ^ swz_rope(srow);
+  // transposing-read offsets of the mix: feature tile dt = 2*wave + mt,
+  // lane supplies tile row 16g + 8kk + 4rd + (lane%16)/4
+  int pv_off[2][2][2];
+  {
+    const int tau = tau_blk(4 * ((lane >> 4) & 1) + (lane & 3));
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+        for (int rd = 0; rd < 2; rd++) {
+          const int dt = 2 * wave + mt;
+          const int row = 16 * g + 8 * kk + 4 * rd + ((lane & 15) >> 2);
+          pv_off[mt][kk][rd] = row * 1024 + 16 * ((4 * (dt & 3) + (tau >> 1)) ^ swz_lat(row)) +
+                               8 * (tau & 1) + 256 * (dt >> 2);
+        }
+  }
+
+  floatx16 acc[2][4];  // mix accumulators [feature tile][head tile]
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = floatx16{};
+  float m = -INFINITY;  // owner waves: running max of scale*log2(e)*score
+  float l = 0.f;        // owner waves: this lane's share of the running sum
+  const float sl2 = p.scale * LOG2E;
+  const int my_loads = TILE / NWAVES + (wave < 4 ? 1 : 0);
+
+  for (int it = 0; it < ntiles; it++) {
+    const int row0 = row_begin + it * TILE;
+    const char* buf = tiles + (it & 1) * BUF_BYTES;
+    if (it + 1 < ntiles) {
+      issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row0 + TILE, row_end,
+                         row_begin, tiles_addr + ((it + 1) & 1) * BUF_BYTES, wave, lane);
+      if (my_loads == 5)
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();  // tile `it` is in LDS; the previous tile's mix is done
+
+    // ---- partial scores over this wave's feature half ------------------------
+    floatx16 sacc = {};
+    {
+      auto score_a = [&](int ks) -> u32x4 {
+        if (ks < D_C / 16)
+          return *reinterpret_cast<const u32x4*>(buf + s_lat + (((2 * (ks & 7)) ^ s_lat_x) << 4) +
+                                                 256 * (ks >> 3));
+        return *reinterpret_cast<const u32x4*>(buf + s_rope +
+                                               (((2 * (ks - D_C / 16)) ^ s_rope_x) << 4));
+      };
+      if (kh == 0) {
+#pragma unroll
+        for (int j = 0; j < QK_STEPS; j++) sacc = mfma32x32x16(as_bf16x8(score_a(j)), q[j], sacc);
+      } else {
+#pragma unroll
+        for (int j = 0; j < QK_STEPS; j++)
+          sacc = mfma32x32x16(as_bf16x8(score_a(QK_STEPS + j)), q[j], sacc);
+      }
+    }
+    if (kh == 0) {
+      float4* dstx = reinterpret_cast<float4*>(sx) + hq * 256 + lane;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++)
+        dstx[64 * j4] = make_float4(sacc[4 * j4], sacc[4 * j4 + 1], sacc[4 * j4 + 2], sacc[4 * j4 + 3]);
+    }
+    __syncthreads();  // partial scores published
+
+    // ---- online softmax (owner waves, log2 domain) -----------------------------
+    if (kh == 1) {
+      const float4* srcx = reinterpret_cast<const float4*>(sx) + hq * 256 + lane;
+      const int valid = row_end - row0;  // rows of this tile that exist
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const float4 o = srcx[64 * j4];
+        const float other[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = 4 * j4 + i;
+          const float t = (sacc[r] + other[i]) * sl2;
+          sacc[r] = (16 * g + r < valid) ? t : -INFINITY;
+          tmax = fmaxf(tmax, sacc[r]);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // lanes n and n+32 share a head
+      int rescaled = 0;
+      float f = 1.f;
+      if (__any(tmax > m + RESCALE_SLACK)) {
+        const float m_new = fmaxf(m, tmax);
+        f = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
+        l *= f;
+        m = m_new;
+        rescaled = 1;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        u32x4 P;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; w2++) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[8 * kk + 2 * w2] - m);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[8 * kk + 2 * w2 + 1] - m);
+          P[w2] = pack_bf16x2(p0, p1);
+          // the denominator sums the rounded weights the mix actually uses
+          l += __uint_as_float(P[w2] << 16) + __uint_as_float(P[w2] & 0xFFFF0000u);
+        }
+        pb[(hq * 2 + kk) * 64 + lane] = P;
+      }
+      if (g == 0) fac[hq * 32 + n] = f;
+      if (lane == 0) flag[hq] = rescaled;
+    }
+    __syncthreads();  // P and rescale factors published
+
+    // ---- probability-weighted latent: features 64w..64w+63, all heads --------
+    {
+#pragma unroll
+      for (int nt = 0; nt < 4; nt++) {
+        if (flag[nt]) {
+          const float fn = fac[nt * 32 + n];
+          acc[0][nt] *= fn;
+          acc[1][nt] *= fn;
+        }
+      }
+      bf16x8 A[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+          A[mt][kk] = tr_pair(buf + pv_off[mt][kk][0], buf + pv_off[mt][kk][1]);
+#pragma unroll
+      for (int nt = 0; nt < 4; nt++) {
+        const bf16x8 B0 = as_bf16x8(pb[(nt * 2 + 0) * 64 + lane]);
+        const bf16x8 B1 = as_bf16x8(pb[(nt * 2 + 1) * 64 + lane]);
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+          acc[mt][nt] = mfma32x32x16(A[mt][0], B0, acc[mt][nt]);
+          acc[mt][nt] = mfma32x32x16(A[mt][1], B1, acc[mt][nt]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue -----------------------------------------------------------------
+  const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
+  if (kh == 1) {
+    const float l_tot = l + __shfl_xor(l, 32);
+    if (g == 0) linv[hq * 32 + n] = 1.f / l_tot;
+    if (g == 0 && head < p.n_h) {
+      const float lse_v = (m + log2f(l_tot)) * LN2;  // natural log of sum exp(z)
+      const int64_t bh = static_cast<int64_t>(b) * p.n_h + head;
+      if (p.num_splits == 1) {
+        if (p.lse) p.lse[bh] = lse_v;
+      } else {
+        p.ws_lse[static_cast<int64_t>(s) * BH + bh] = lse_v;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* out_base = p.num_splits == 1
+                           ? static_cast<uint16_t*>(p.out_lat)
+                           : static_cast<uint16_t*>(p.ws_o) + static_cast<int64_t>(s) * BH * D_C;
+#pragma unroll
+  for (int nt = 0; nt < 4; nt++) {
+    const int h = hg * 128 + nt * 32 + n;
+    if (h >= p.n_h) continue;
+    const float inv = linv[nt * 32 + n];
+    uint16_t* dst = out_base + (static_cast<int64_t>(b) * p.n_h + h) * D_C;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      u32x4 v0, v1;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; w2++) {
+        v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2] * inv, acc[mt][nt][2 * w2 + 1] * inv);
+        v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2] * inv, acc[mt][nt][8 + 2 * w2 + 1] * inv);
+      }
+      uint16_t* o = dst + 64 * wave + 32 * mt + 16 * g;
+      st16(o, v0);
+      st16(o + 8, v1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of split partials: one 64-lane block per (b, h), 8 features per lane
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_bits_to_float(p[i]);
+}
+__device__ __forceinline__ void st_elem(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_elem(uint16_t* p, int64_t i, float v) {
+  p[i] = float_to_bf16_bits(v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void merge_splits_kernel(const T* __restrict__ ws_o,
+                                                          const float* __restrict__ ws_lse,
+                                                          int S, int64_t BH, T* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; s++) mx = fmaxf(mx, ws_lse[s * BH + bh]);
+  float wsum = 0.f;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int c0 = threadIdx.x * 8;
+  for (int s = 0; s < S; s++) {
+    const float w = __expf(ws_lse[s * BH + bh] - mx);
+    wsum += w;
+    const T* src = ws_o + (s * BH + bh) * D_C + c0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = fmaf(w, ld_elem<T>(src, i), acc[i]);
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int i = 0; i < 8; i++) st_elem(out, bh * D_C + c0 + i, acc[i] * inv);
+  if (threadIdx.x == 0 && lse) lse[bh] = mx + logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 decode: one block of 256 threads per (b, h, split)
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
+  __shared__ float qs[D_QK];
+  __shared__ float ps[256];
+  __shared__ int ts[256];
+  __shared__ float red[8];
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t bh = static_cast<int64_t>(b) * p.n_h + h;
+  const float* ql = static_cast<const float*>(p.q_lat) + bh * D_C;
+  const float* qp = static_cast<const float*>(p.q_pe) + bh * D_R;
+  for (int c = tid; c < D_QK; c += 256) qs[c] = c < D_C ? ql[c] : qp[c - D_C];
+  const float* lat = static_cast<const float*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs;
+  const float* rp = static_cast<const float*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs;
+  const int row_begin = s * p.tiles_per_split * TILE;
+  const int row_end = min(p.rows, row_begin + p.tiles_per_split * TILE);
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int r0 = row_begin; r0 < row_end; r0 += 256) {
+    const int rr = r0 + tid;
+    float t = -INFINITY;
+    int tok = 0;
+    if (rr < row_end) {
+      tok = p.idx ? p.idx[static_cast<int64_t>(b) * p.K + rr] : rr;
+      const float* lrow = lat + static_cast<int64_t>(tok) * p.lat_rs;
+      const float* rrow = rp + static_cast<int64_t>(tok) * p.rope_rs;
+      float content = 0.f, rotary = 0.f;
+      for (int c = 0; c < D_C; c++) content = fmaf(qs[c], lrow[c], content);
+      for (int c = 0; c < D_R; c++) rotary = fmaf(qs[D_C + c], rrow[c], rotary);
+      t = p.scale * (content + rotary);
+    }
+    // block max
+    float v = t;
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    const float tmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float m_new = fmaxf(m, tmax);
+    const float f = expf(m - m_new);
+    const float pv = rr < row_end ? expf(t - m_new) : 0.f;
+    ps[tid] = pv;
+    ts[tid] = tok;
+    float sv = pv;
+    for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = sv;
+    __syncthreads();
+    l = l * f + (red[4] + red[5] + red[6] + red[7]);
+    acc0 *= f;
+    acc1 *= f;
+    m = m_new;
+    const int nr = min(256, row_end - r0);
+    for (int j = 0; j < nr; j++) {
+      const float* lrow = lat + static_cast<int64_t>(ts[j]) * p.lat_rs;
+      acc0 = fmaf(ps[j], lrow[tid], acc0);
+      acc1 = fmaf(ps[j], lrow[tid + 256], acc1);
+    }
+    __syncthreads();
+  }
+  float* dst;
+  float* lse_dst;
+  if (p.num_splits == 1) {
+    dst = static_cast<float*>(p.out_lat) + bh * D_C;
+    lse_dst = p.lse ? p.lse + bh : nullptr;
+  } else {
+    const int64_t sbh = static_cast<int64_t>(s) * p.B * p.n_h + bh;
+    dst = static_cast<float*>(p.ws_o) + sbh * D_C;
+    lse_dst = p.ws_lse + sbh;
+  }
+  dst[tid] = acc0 / l;
+  dst[tid + 256] = acc1 / l;
+  if (tid == 0 && lse_dst) *lse_dst = m + logf(l);
+}
+
+hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream) {
+  const int hgroups = (p.n_h + 127) / 128;
+  if (is_bf16) {
+    dim3 grid(p.num_splits, hgroups, p.B);
+    if (p.idx)
+      hipLaunchKernelGGL(decode_bf16_kernel<true>, grid, dim3(NWAVES * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(decode_bf16_kernel<false>, grid, dim3(NWAVES * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_f32_kernel, dim3(p.num_splits, p.n_h, p.B), dim3(256), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.num_splits == 1) return e;
+  const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
+  if (is_bf16)
+    hipLaunchKernelGGL(merge_splits_kernel<uint16_t>, dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+                       stream, static_cast<const uint16_t*>(p.ws_o), p.ws_lse, p.num_splits, BH,
+                       static_cast<uint16_t*>(p.out_lat), p.lse);
+  else
+    hipLaunchKernelGGL(merge_splits_kernel<float>, dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+                       stream, static_cast<const float*>(p.ws_o), p.ws_lse, p.num_splits, BH,
+                       static_cast<float*>(p.out_lat), p.lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,43 @@
+// launch.hpp — internal kernel launchers of libmla (arguments already checked).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+hipError_t launch_dequant_fp8_block(const uint8_t* w, const float* scale, int64_t rows,
+                                    int64_t cols, uint16_t* out, hipStream_t stream);
+
+// is_bf16: element type of q_nope / wkv_b / q_lat (else float32)
+hipError_t launch_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, int B, int n_h,
+                           bool is_bf16, hipStream_t stream);
+
+hipError_t launch_out_up(const void* o_lat, const void* wkv_b, void* out, int B, int n_h,
+                         bool is_bf16, hipStream_t stream);
+
+hipError_t launch_kv_reconstruct(const void* c, const void* k_rope, const void* wkv_b, void* K,
+                                 void* V, int64_t N, int n_h, bool is_bf16, hipStream_t stream);
+
+struct DecodeParams {
+  const void* q_lat;
+  const void* q_pe;
+  const void* latent;
+  const void* rope;
+  int64_t lat_bs, lat_rs, rope_bs, rope_rs;  // element strides
+  int B, n_h, T;
+  const int32_t* idx;  // nullptr = dense
+  int K;
+  int rows;            // attended positions per sequence (T or K)
+  int num_splits;
+  int tiles_per_split; // 32-row tiles per split
+  float scale;
+  void* out_lat;
+  float* lse;
+  void* ws_o;          // [num_splits, B, n_h, 512] partial outputs (split > 1)
+  float* ws_lse;       // [num_splits, B, n_h]
+};
+
+hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,86 @@
+// out_up.hip — W^UV applied after the probability-weighted latent sum.
+//
+// Operation ("KV Reconstruction", How it works, second absorb identity and
+// Watch-outs: attend on the latent, then apply W^UV; "Absorb key weights",
+// decode excerpt, last einsum; "Value up-projection", Explanation: value rows
+// are 128..255 of each head's 256):
+//   out[b,h,d] = sum_c out_lat[b,h,c] * wkv_b[h*256 + 128 + d, c]
+//
+// Per head a [B x 512] x [512 x 128] product bound by streaming the 16 MiB of
+// W^UV. Here the contraction runs along W's contiguous axis, so both MFMA
+// operands are straight 16-byte loads: one wave per (head, 32-wide value
+// tile, 32-row batch tile), v_mfma_f32_32x32x16_bf16 with M = batch rows,
+// N = value features, K = latent features.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+__global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __restrict__ o_lat,
+                                                          const uint16_t* __restrict__ w,
+                                                          uint16_t* __restrict__ out, int B,
+                                                          int n_h) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int nbt = (B + 31) >> 5;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= n_h * 4 * nbt) return;
+  const int bt = gw % nbt;
+  const int dt = (gw / nbt) & 3;
+  const int h = gw / (nbt * 4);
+  const int b = bt * 32 + n;
+  const int d = dt * 32 + n;  // this lane's B-operand column (value feature)
+  const uint16_t* orow = o_lat + (static_cast<int64_t>(b) * n_h + h) * D_C;
+  const uint16_t* wrow = w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C;
+
+  floatx16 acc0 = {}, acc1 = {};
+#pragma unroll 4
+  for (int ks = 0; ks < D_C / 16; ks += 2) {
+    const int c0 = ks * 16 + g * 8;
+    u32x4 a0 = (b < B) ? ld16(orow + c0) : u32x4{0, 0, 0, 0};
+    u32x4 a1 = (b < B) ? ld16(orow + c0 + 16) : u32x4{0, 0, 0, 0};
+    u32x4 w0 = ld16(wrow + c0);
+    u32x4 w1 = ld16(wrow + c0 + 16);
+    acc0 = mfma32x32x16(as_bf16x8(a0), as_bf16x8(w0), acc0);
+    acc1 = mfma32x32x16(as_bf16x8(a1), as_bf16x8(w1), acc1);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int bo = bt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    if (bo < B)
+      out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(acc0[r] + acc1[r]);
+  }
+}
+
+// fp32: one block per (b, h); thread d walks its W^UV row.
+__global__ __launch_bounds__(128) void out_up_f32_kernel(const float* __restrict__ o_lat,
+                                                         const float* __restrict__ w,
+                                                         float* __restrict__ out, int n_h) {
+  __shared__ float o[D_C];
+  const int bh = blockIdx.x;
+  const int h = bh % n_h;
+  for (int c = threadIdx.x; c < D_C; c += 128) o[c] = o_lat[static_cast<int64_t>(bh) * D_C + c];
+  __syncthreads();
+  const int d = threadIdx.x;
+  const float* wrow = w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C;
+  float acc = 0.f;
+  for (int c = 0; c < D_C; c++) acc = fmaf(o[c], wrow[c], acc);
+  out[static_cast<int64_t>(bh) * D_V + d] = acc;
+}
+
+hipError_t launch_out_up(const void* o_lat, const void* wkv_b, void* out, int B, int n_h,
+                         bool is_bf16, hipStream_t stream) {
+  if (is_bf16) {
+    const int waves = n_h * 4 * ((B + 31) / 32);
+    hipLaunchKernelGGL(out_up_bf16_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(wkv_b),
+                       static_cast<uint16_t*>(out), B, n_h);
+  } else {
+    hipLaunchKernelGGL(out_up_f32_kernel, dim3(static_cast<unsigned>(B) * n_h), dim3(128), 0,
+                       stream, static_cast<const float*>(o_lat), static_cast<const float*>(wkv_b),
+                       static_cast<float*>(out), n_h);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

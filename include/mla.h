@@ -136,9 +136,10 @@ int mla_decode_num_splits(int B, int n_h, int T, int K);
  *          duplicates are counted twice; callers must guarantee the contract.
  *   out_lat [B, n_h, 512] (dt, out), lse [B, n_h] float32 (out, or NULL).
  *   num_splits  number of partitions of the attended positions (0 = let the
- *          library choose; otherwise 1 <= num_splits <= ceil(rows/32), where
- *          rows = T, or K with topk_idx). Results differ between split counts
- *          only by floating-point rounding.
+ *          library choose; otherwise lo <= num_splits <= ceil(rows/32), where
+ *          rows = T, or K with topk_idx, and lo = 1 dense, ceil(K/1024) with
+ *          topk_idx). Results differ between split counts only by
+ *          floating-point rounding.
  *   workspace  device memory of at least
  *          mla_decode_workspace_bytes(B, n_h, T, K, num_splits, dt) bytes
  *          (may be NULL when that is 0).

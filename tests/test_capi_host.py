@@ -1,0 +1,124 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, and rejects bad arguments on the host before any HIP
+call (null pointers, bad sizes, bad index counts, short workspace)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_latent_attention_mla_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
+                     "mla_out_up", "mla_kv_reconstruct", "mla_decode_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_str(OK) == b"MLA_OK"
+    assert lib.mla_status_str(WORKSPACE) == b"MLA_ERR_WORKSPACE"
+
+
+def test_dequant_argument_errors(lib):
+    s = None
+    assert lib.mla_dequant_fp8_block(None, FAKE, 4, 16, FAKE, s) == INVALID
+    assert lib.mla_dequant_fp8_block(FAKE, FAKE, -1, 16, FAKE, s) == INVALID
+    assert lib.mla_dequant_fp8_block(FAKE, FAKE, 4, 17, FAKE, s) == UNSUPPORTED
+    assert lib.mla_dequant_fp8_block(None, None, 0, 16, None, s) == OK  # empty: no-op
+    assert b"null" in lib.mla_last_error() or lib.mla_last_error() is not None
+
+
+def test_absorb_and_out_up_argument_errors(lib):
+    for fn in (lib.mla_absorb_q, lib.mla_out_up):
+        assert fn(None, FAKE, FAKE, 2, 16, BF16, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, -1, 16, BF16, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, 2, 0, BF16, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, 2, 16, 7, None) == INVALID
+        assert fn(None, None, None, 0, 16, BF16, None) == OK
+        assert fn(ctypes.c_void_p(0x10002), FAKE, FAKE, 2, 16, BF16, None) == UNSUPPORTED
+
+
+def decode(lib, **kw):
+    a = dict(q_lat=FAKE, q_pe=FAKE, latent=FAKE, rope=FAKE, lbs=4096 * 576, lrs=576,
+             rbs=4096 * 576, rrs=576, B=2, n_h=128, T=4096, idx=None, K=0, scale=0.07,
+             splits=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.mla_decode_latent_attn(a["q_lat"], a["q_pe"], a["latent"], a["rope"], a["lbs"],
+                                      a["lrs"], a["rbs"], a["rrs"], a["B"], a["n_h"], a["T"],
+                                      a["idx"], a["K"], a["scale"], a["splits"], a["out"],
+                                      a["lse"], a["ws"], a["ws_bytes"], a["dt"], a["stream"])
+
+
+def test_decode_argument_errors(lib):
+    assert decode(lib, q_lat=None) == INVALID
+    assert decode(lib, n_h=0) == INVALID
+    assert decode(lib, T=0) == INVALID
+    assert decode(lib, B=-3) == INVALID
+    assert decode(lib, idx=FAKE, K=0) == INVALID          # empty top-k set
+    assert decode(lib, idx=FAKE, K=4097) == INVALID       # K > T
+    assert decode(lib, lrs=500) == INVALID                # row stride below 512
+    assert decode(lib, rrs=60) == INVALID
+    assert decode(lib, lrs=580) == UNSUPPORTED            # not a multiple of 8 elements
+    assert decode(lib, splits=-1) == INVALID
+    assert decode(lib, splits=129) == INVALID             # more splits than 32-row tiles
+    assert decode(lib, scale=float("nan")) == INVALID
+    assert decode(lib, ws=None) == WORKSPACE
+    assert decode(lib, ws_bytes=16) == WORKSPACE
+    assert decode(lib, dt=5) == INVALID
+    assert decode(lib, B=0, q_lat=None) == OK              # empty batch: no-op
+
+
+def test_workspace_size_queries(lib):
+    ws = binding.mla_decode_workspace_bytes
+    assert ws(32, 128, 4096) > 0
+    assert ws(256, 128, 4096) == 0  # enough workgroups without splitting
+    assert ws(1, 128, 32, num_splits=1) == 0
+    # grows with the split count
+    assert ws(2, 128, 4096, num_splits=8) < ws(2, 128, 4096, num_splits=16)
+    with pytest.raises(binding.MLAError):
+        ws(2, 128, 4096, K=5000)
+    assert binding.mla_decode_num_splits(32, 128, 4096) == 8
+    assert binding.mla_decode_num_splits(4, 128, 32768) == 64
+    assert binding.mla_decode_num_splits(8, 128, 65536, 2048) == 32
+    assert binding.mla_decode_num_splits(1, 16, 1) == 1
+
+
+def test_reconstruct_argument_errors(lib):
+    s = None
+    assert lib.mla_kv_reconstruct(None, FAKE, FAKE, FAKE, FAKE, 8, 16, BF16, s) == INVALID
+    assert lib.mla_kv_reconstruct(FAKE, FAKE, FAKE, FAKE, FAKE, -8, 16, BF16, s) == INVALID
+    assert lib.mla_kv_reconstruct(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0, BF16, s) == INVALID
+    assert lib.mla_kv_reconstruct(None, None, None, None, None, 0, 16, BF16, s) == OK
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding.mla_absorb_q(torch.zeros(1, 16, 128, dtype=torch.bfloat16),
+                             torch.zeros(16 * 256, 512, dtype=torch.bfloat16))

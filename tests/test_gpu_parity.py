@@ -1,0 +1,320 @@
+"""GPU parity: every HIP entry point against the fp64 CPU oracle.
+
+Both sides get the same seeded, stored inputs (bf16 or fp32 tensors from
+head_latent_attention_mla_amd.synth). Tolerances: max|err| <= 2e-2 * max|ref|
+for bf16 paths, <= 1e-5 * max|ref| for fp32, bit-exact for the fp8
+dequantisation and for the k^R copy inside K. Sizes span several tiles and
+ragged tails; the five workloads run at full size (the reconstruction is
+checked on sampled tokens).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_latent_attention_mla_amd import binding as mla
+from head_latent_attention_mla_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+DEV = "cuda:0"
+
+
+def check(got, ref, tol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    assert err <= tol * scale, f"{what}: max|err| {err:.3e} > {tol} * max|ref| {scale:.3e}"
+
+
+def host(t):
+    return t.detach().cpu()
+
+
+def f64(t):
+    t = host(t)
+    return t.double().numpy()
+
+
+def cuda(t):
+    return t.to(DEV)
+
+
+# --------------------------------------------------------------------------
+# FP8 block dequantisation: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(512, 4096), (300, 272), (1, 16), (129, 144)])
+def test_dequant_bit_exact(rows, cols):
+    codes = synth.fp8_codes(rows, cols, seed=rows * 7 + cols)
+    g = np.random.default_rng(rows + cols)
+    scales = (g.uniform(0.5, 2.0, ((rows + 127) // 128, (cols + 127) // 128)) * 2.0 ** -4
+              ).astype(np.float32)
+    out = mla.mla_dequant_fp8_block(cuda(codes), cuda(torch.from_numpy(scales)))
+    got = host(out).view(torch.int16).numpy().view(np.uint16)
+    ref = oracle.dequant_fp8_block(codes.numpy(), scales)
+    assert np.array_equal(got, ref)
+
+
+def test_dequant_every_code_with_unit_scale():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(128, 1)  # [128, 256]
+    codes[(codes & 0x7F) == 0x7F] = 0  # NaN codes: payload unspecified, excluded
+    scales = torch.ones((1, 2), dtype=torch.float32)
+    got = host(mla.mla_dequant_fp8_block(cuda(codes), cuda(scales)))
+    got = got.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.dequant_fp8_block(codes.numpy(), scales.numpy()))
+
+
+def test_dequant_nan_codes_give_nan():
+    codes = torch.full((1, 16), 0x7F, dtype=torch.uint8)
+    codes[0, 1::2] = 0xFF
+    got = host(mla.mla_dequant_fp8_block(cuda(codes), cuda(torch.ones((1, 1)))))
+    assert torch.isnan(got.float()).all()
+
+
+# --------------------------------------------------------------------------
+# absorb and W^UV stages
+# --------------------------------------------------------------------------
+
+STAGE_CASES = [(1, 16, torch.bfloat16), (5, 16, torch.bfloat16), (32, 128, torch.bfloat16),
+               (33, 128, torch.bfloat16), (70, 48, torch.bfloat16), (1, 16, torch.float32),
+               (3, 128, torch.float32)]
+
+
+@pytest.mark.parametrize("B,n_h,dtype", STAGE_CASES)
+def test_absorb_q(B, n_h, dtype):
+    inp = synth.decode_inputs(B, n_h, 1, dtype, seed=B * 100 + n_h)
+    got = mla.mla_absorb_q(cuda(inp["q_nope"]), cuda(inp["wkv_b"]))
+    ref = oracle.absorb_q(inp["q_nope"], inp["wkv_b"])
+    check(f64(got), ref, BF16_TOL if dtype == torch.bfloat16 else F32_TOL, "q_lat")
+
+
+@pytest.mark.parametrize("B,n_h,dtype", STAGE_CASES)
+def test_out_up(B, n_h, dtype):
+    inp = synth.decode_inputs(B, n_h, 1, dtype, seed=B * 100 + n_h + 1, stage_inputs=True)
+    got = mla.mla_out_up(cuda(inp["o_lat"]), cuda(inp["wkv_b"]))
+    ref = oracle.out_up(inp["o_lat"], inp["wkv_b"])
+    check(f64(got), ref, BF16_TOL if dtype == torch.bfloat16 else F32_TOL, "out")
+
+
+# --------------------------------------------------------------------------
+# latent attention stage
+# --------------------------------------------------------------------------
+
+def run_decode(inp, T=None, topk=None, num_splits=0, dtype=None):
+    cache = cuda(inp["cache"])
+    out, lse = mla.mla_decode_latent_attn(
+        cuda(inp["q_lat"]), cuda(inp["q_pe"]), cache[..., :512], cache[..., 512:], T=T,
+        topk_idx=None if topk is None else cuda(topk), num_splits=num_splits, want_lse=True)
+    return out, lse
+
+
+def oracle_decode(inp, T=None, topk=None):
+    cache = inp["cache"]
+    o, lse, _ = oracle.latent_attention(inp["q_lat"], inp["q_pe"], cache[..., :512],
+                                        cache[..., 512:], T=T, topk_idx=topk, want_lse=True)
+    return o, lse
+
+
+DECODE_CASES = [
+    # B, n_h, T, topk K, splits
+    (1, 16, 1, None, 0),
+    (2, 16, 31, None, 0),
+    (3, 128, 100, None, 0),
+    (2, 128, 100, None, 2),
+    (2, 48, 257, None, 3),
+    (1, 256, 64, None, 1),
+    (4, 128, 1000, None, 0),
+    (2, 128, 300, 1, 0),
+    (2, 128, 300, 37, 0),
+    (3, 128, 700, 300, 4),
+    (2, 16, 64, 64, 0),
+]
+
+
+@pytest.mark.parametrize("B,n_h,T,K,splits", DECODE_CASES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_latent_attn(B, n_h, T, K, splits, dtype):
+    seed = B * 1000 + n_h + T
+    inp = synth.decode_inputs(B, n_h, T, dtype, seed=seed, topk=K, stage_inputs=True)
+    topk = inp.get("topk_idx")
+    out, lse = run_decode(inp, topk=topk, num_splits=splits)
+    ref_o, ref_lse = oracle_decode(inp, topk=topk)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    check(f64(out), ref_o, tol, "out_lat")
+    # lse: the bf16 path normalises by the sum of the bf16-rounded weights it
+    # mixes with (each within 2^-9 relative), so |d lse| <= 2^-8 absolute; the
+    # fp32 path keeps fp32 weights.
+    lse_err = np.max(np.abs(host(lse).double().numpy() - ref_lse))
+    assert lse_err <= (2.0 ** -8 if dtype == torch.bfloat16 else 1e-5), lse_err
+
+
+def test_decode_separate_strided_caches():
+    # pages' layout: kv_cache [B_max, T_max, 512] and pe_cache [B_max, T_max, 64]
+    # read as [:B, :T]
+    B, n_h, T, Tmax = 3, 128, 200, 256
+    inp = synth.decode_inputs(4, n_h, Tmax, torch.bfloat16, seed=77, stage_inputs=True)
+    lat = cuda(inp["cache"][..., :512].contiguous())
+    rope = cuda(inp["cache"][..., 512:].contiguous())
+    q_lat = cuda(inp["q_lat"][:B].contiguous())
+    q_pe = cuda(inp["q_pe"][:B].contiguous())
+    out = mla.mla_decode_latent_attn(q_lat, q_pe, lat, rope, T=T)
+    ref, _, _ = oracle.latent_attention(inp["q_lat"][:B], inp["q_pe"][:B],
+                                        inp["cache"][:B, :, :512], inp["cache"][:B, :, 512:],
+                                        T=T)
+    check(f64(out), ref, BF16_TOL, "out_lat")
+
+
+def test_decode_all_ones_latent_gives_ones():
+    # probabilities sum to one inside the fused kernel and across the merge
+    inp = synth.decode_inputs(2, 128, 777, torch.bfloat16, seed=5, stage_inputs=True)
+    inp["cache"][..., :512] = 1.0
+    for splits in (1, 5, 0):
+        out, _ = run_decode(inp, num_splits=splits)
+        assert torch.equal(host(out).float(), torch.ones(2, 128, 512)), splits
+
+
+def test_decode_poisoned_rows_outside_topk_are_never_used():
+    inp = synth.decode_inputs(2, 128, 500, torch.bfloat16, seed=6, topk=50, stage_inputs=True)
+    topk = inp["topk_idx"]
+    out_a, lse_a = run_decode(inp, topk=topk)
+    poisoned = dict(inp, cache=inp["cache"].clone())
+    for b in range(2):
+        keep = torch.zeros(500, dtype=torch.bool)
+        keep[topk[b].long()] = True
+        poisoned["cache"][b, ~keep, :256] = float("nan")
+        poisoned["cache"][b, ~keep, 256:] = 1e30
+    out_b, lse_b = run_decode(poisoned, topk=topk)
+    assert torch.equal(host(out_a), host(out_b)) and torch.equal(host(lse_a), host(lse_b))
+
+
+def test_decode_split_count_changes_only_rounding():
+    inp = synth.decode_inputs(2, 128, 2048, torch.bfloat16, seed=7, stage_inputs=True)
+    ref_o, _ = oracle_decode(inp)
+    outs = []
+    for splits in (1, 2, 4, 16, 64, 0):
+        out, _ = run_decode(inp, num_splits=splits)
+        check(f64(out), ref_o, BF16_TOL, f"splits={splits}")
+        outs.append(f64(out))
+    for o in outs[1:]:
+        check(o, outs[0], BF16_TOL, "split vs single")
+
+
+def test_decode_is_deterministic():
+    inp = synth.decode_inputs(4, 128, 1500, torch.bfloat16, seed=8, stage_inputs=True)
+    a, la = run_decode(inp)
+    b, lb = run_decode(inp)
+    assert torch.equal(host(a), host(b)) and torch.equal(host(la), host(lb))
+
+
+def test_decode_full_topk_equals_dense():
+    inp = synth.decode_inputs(2, 128, 96, torch.bfloat16, seed=9, stage_inputs=True)
+    perm = torch.stack([torch.randperm(96, generator=torch.Generator().manual_seed(b))
+                        for b in range(2)]).int()
+    dense, _ = run_decode(inp)
+    sparse, _ = run_decode(inp, topk=perm)
+    check(f64(sparse), f64(dense), BF16_TOL, "K=T sparse vs dense")
+
+
+def test_decode_empty_batch_is_noop():
+    q = torch.empty((0, 128, 512), dtype=torch.bfloat16, device=DEV)
+    qp = torch.empty((0, 128, 64), dtype=torch.bfloat16, device=DEV)
+    cache = torch.zeros((1, 4, 576), dtype=torch.bfloat16, device=DEV)
+    out = mla.mla_decode_latent_attn(q, qp, cache[..., :512], cache[..., 512:], T=4)
+    assert out.shape == (0, 128, 512)
+
+
+# --------------------------------------------------------------------------
+# naive reconstruction
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,n_h,dtype", [(1, 16, torch.bfloat16), (100, 16, torch.bfloat16),
+                                         (300, 128, torch.bfloat16), (257, 48, torch.bfloat16),
+                                         (37, 16, torch.float32), (5, 128, torch.float32)])
+def test_kv_reconstruct(N, n_h, dtype):
+    inp = synth.reconstruct_inputs(N, n_h, dtype, seed=N + n_h)
+    K, V = mla.mla_kv_reconstruct(cuda(inp["c"]), cuda(inp["k_rope"]), cuda(inp["wkv_b"]))
+    Kr, Vr = oracle.kv_reconstruct(inp["c"], inp["k_rope"], inp["wkv_b"], n_h)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    check(f64(K)[..., :128], Kr[..., :128], tol, "k_nope")
+    check(f64(V), Vr, tol, "v")
+    # the rotary part is a copy of k^R for every head, bit for bit
+    assert torch.equal(host(K)[..., 128:], inp["k_rope"][:, None, :].expand(N, n_h, 64))
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=1)
+def config_inputs(cfg):
+    return synth.config_inputs(cfg)
+
+
+def gpu_decode_step(inp, wkv_b, topk=None):
+    cache = cuda(inp["cache"])
+    q_lat = mla.mla_absorb_q(cuda(inp["q_nope"]), wkv_b)
+    o_lat = mla.mla_decode_latent_attn(q_lat, cuda(inp["q_pe"]), cache[..., :512],
+                                       cache[..., 512:],
+                                       topk_idx=None if topk is None else cuda(topk))
+    return mla.mla_out_up(o_lat, wkv_b)
+
+
+def test_config1_tiny_fp32_both_paths():
+    inp = config_inputs(1)
+    cache = inp["cache"]
+    w = inp["wkv_b"]
+    out = gpu_decode_step(inp, cuda(w))
+    ref_abs = oracle.decode_absorbed(inp["q_nope"], inp["q_pe"], cache[..., :512],
+                                     cache[..., 512:], w)["out"]
+    ref_naive = oracle.decode_naive(inp["q_nope"], inp["q_pe"], cache[..., :512],
+                                    cache[..., 512:], w)["out"]
+    check(f64(out), ref_abs, F32_TOL, "absorbed")
+    check(f64(out), ref_naive, F32_TOL, "naive")
+    # the naive path's reconstruction of the cached rows on the GPU
+    K, V = mla.mla_kv_reconstruct(cuda(cache[0, :, :512].contiguous()),
+                                  cuda(cache[0, :, 512:].contiguous()), cuda(w))
+    Kr, Vr = oracle.kv_reconstruct(cache[0, :, :512], cache[0, :, 512:], w, 16)
+    check(f64(K), Kr, F32_TOL, "K")
+    check(f64(V), Vr, F32_TOL, "V")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_config_dense_full_step(cfg):
+    inp = config_inputs(cfg)
+    out = gpu_decode_step(inp, cuda(inp["wkv_b"]))
+    cache = inp["cache"]
+    ref = oracle.decode_absorbed(inp["q_nope"], inp["q_pe"], cache[..., :512],
+                                 cache[..., 512:], inp["wkv_b"])["out"]
+    check(f64(out), ref, BF16_TOL, f"config {cfg}")
+
+
+def test_config4_sparse_fp8_full_step():
+    inp = config_inputs(4)
+    w = mla.mla_dequant_fp8_block(cuda(inp["wkv_b_fp8"]), cuda(inp["wkv_b_scale"]))
+    w_ref = oracle.dequant_fp8_block(inp["wkv_b_fp8"].numpy(), inp["wkv_b_scale"].numpy())
+    assert np.array_equal(host(w).view(torch.int16).numpy().view(np.uint16), w_ref)
+    out = gpu_decode_step(inp, w, topk=inp["topk_idx"])
+    cache = inp["cache"]
+    ref = oracle.decode_absorbed(inp["q_nope"], inp["q_pe"], cache[..., :512],
+                                 cache[..., 512:], w_ref, topk_idx=inp["topk_idx"])["out"]
+    check(f64(out), ref, BF16_TOL, "config 4")
+
+
+def test_config5_reconstruct_sampled_tokens():
+    inp = config_inputs(5)
+    K, V = mla.mla_kv_reconstruct(cuda(inp["c"]), cuda(inp["k_rope"]), cuda(inp["wkv_b"]))
+    rows = np.sort(np.random.default_rng(5).choice(8192, 48, replace=False))
+    rows = np.concatenate([[0, 255, 256, 8191], rows])
+    Kr, Vr = oracle.kv_reconstruct(inp["c"][rows], inp["k_rope"][rows], inp["wkv_b"], 128)
+    Kg, Vg = host(K)[rows], host(V)[rows]
+    check(Kg[..., :128].double().numpy(), Kr[..., :128], BF16_TOL, "k_nope")
+    check(Vg.double().numpy(), Vr, BF16_TOL, "v")
+    assert torch.equal(host(K)[..., 128:], inp["k_rope"][:, None, :].expand(8192, 128, 64))
