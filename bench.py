@@ -41,6 +41,8 @@ def parse():
                     help="decode workload (2: B=32 T=4096; 3: B=4 T=32768; 4: sparse fp8)")
     ap.add_argument("--min-replica-bytes", type=float, default=1.1e9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     return ap.parse_args()
 
 
@@ -173,21 +175,41 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: whole steps, bracketed by synchronisation
+    # eager pass: events around each call (per-call durations, dominant kernel)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    absorb_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    outup_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    eager_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+
+    # timed region: whole steps replayed from HIP graphs (one per replica),
+    # bracketed by synchronisation
+    graphs = []
+    if not args.no_graph:
+        for r in range(R):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                step(r)
+            graphs.append(gph)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        if graphs:
+            graphs[i % R].replay()
+        else:
+            step(i)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    absorb_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    outup_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
     work = algorithmic_work(B, n_h, rows)
     value = B * rows * n_h / (ms_step * 1e-3)
@@ -221,6 +243,8 @@ def main():
                  "bytes": work["step_bytes"], "flops": work["step_flops"],
                  "GB_s": work["step_bytes"] / (ms_step * 1e-3) / 1e9,
                  "TFLOP_s": work["step_flops"] / (ms_step * 1e-3) / 1e12,
+                 "launch": "eager" if args.no_graph else "hip_graph_replay",
+                 "eager_step_us": eager_ms * 1e3,
                  "absorb_us": absorb_ms * 1e3, "decode_us": decode_ms * 1e3,
                  "out_up_us": outup_ms * 1e3},
         "published_baseline": "none: the source pages print no throughput figures",

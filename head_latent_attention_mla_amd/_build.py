@@ -17,6 +17,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # register-pressure-aware scheduling: keeps the decode kernel's tile loop
+    # free of scratch spills (whose reloads would drain the tile DMA)
+    "-mllvm", "-amdgpu-use-amdgpu-trackers=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

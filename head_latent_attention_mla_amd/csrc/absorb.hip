@@ -5,17 +5,19 @@
 //   q_lat[b,h,c] = sum_{d<128} q_nope[b,h,d] * wkv_b[h*256 + d, c]
 //
 // Per head this is a [B x 128] x [128 x 512] product; the 16 MiB of W^UK
-// (n_h = 128, bf16) dominates the bytes, so the kernel is built to stream W
-// once with wide loads and keep the contraction on MFMA.
+// (n_h = 128, bf16) dominates the bytes, so the kernel is built to have all
+// of W in flight at once and keep the contraction on MFMA.
 //
-// bf16 path: one wave per (head, 128-column quarter, 32-row batch tile),
-// v_mfma_f32_32x32x16_bf16 with M = batch rows, N = latent columns,
-// K = content features d. The contraction runs along W's row axis (its
-// stride), so each lane loads 8 consecutive W rows x 4 consecutive columns
-// (8-byte loads) and transposes that 8x4 block in registers into the B
-// operands of four N-tiles. Tile j's column n is latent column 4n + j, which
-// makes each lane's four accumulators four adjacent output columns: one
-// 8-byte store per output row.
+// bf16 path: one workgroup of 4 waves per (head, 128-column quarter, 32-row
+// batch tile); wave w takes the content features d in [32w, 32w+32) (two
+// k-steps of v_mfma_f32_32x32x16_bf16 with M = batch rows, N = latent
+// columns) and issues all of its loads before the first multiply. The
+// contraction runs along W's row axis (its stride), so each lane loads 8
+// consecutive W rows x 4 consecutive columns (8-byte loads) per k-step and
+// transposes that 8x4 block in registers into the B operands of four
+// N-tiles; tile j's column n is latent column 4n + j, which makes each
+// lane's four accumulators four adjacent output columns. The four partial
+// sums meet in LDS and wave 0 stores 8-byte rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,41 +34,71 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ w,
                                                             uint16_t* __restrict__ q_lat, int B,
                                                             int n_h) {
-  const int lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) floatx4 red[3][4][4][64];  // waves 1..3 partials
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
   const int nbt = (B + 31) >> 5;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave id
-  if (gw >= n_h * 4 * nbt) return;
-  const int bt = gw % nbt;
-  const int cq = (gw / nbt) & 3;
-  const int h = gw / (nbt * 4);
-  const int b = bt * 32 + n;  // this lane's A-operand row
+  const int bt = blockIdx.x % nbt;
+  const int cq = (blockIdx.x / nbt) & 3;
+  const int h = blockIdx.x / (nbt * 4);
+  // rows past B load row B-1 (unconditional loads keep all of them in
+  // flight); their results are never stored
+  const int b = min(bt * 32 + n, B - 1);  // this lane's A-operand row
   const int col0 = cq * 128 + 4 * n;
   const uint16_t* wh = w + static_cast<int64_t>(h) * ROWS_PER_HEAD * D_C + col0;
   const uint16_t* qrow = q_nope + (static_cast<int64_t>(b) * n_h + h) * D_N;
 
-  floatx16 acc[4];
-  for (int j = 0; j < 4; j++) acc[j] = floatx16{};
-#pragma unroll 2
-  for (int ks = 0; ks < D_N / 16; ks++) {
-    const int d0 = ks * 16 + g * 8;
-    u32x4 a = (b < B) ? ld16(qrow + d0) : u32x4{0, 0, 0, 0};
-    u32x2 e[8];
+  // all loads of this wave up front: 2 k-steps x (A: 16 bytes, B: 8 rows x 8 bytes)
+  u32x4 a[2];
+  u32x2 e[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const int d0 = wave * 32 + k * 16 + g * 8;
+    a[k] = ld16(qrow + d0);
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      e[i] = *reinterpret_cast<const u32x2*>(wh + static_cast<int64_t>(d0 + i) * D_C);
-    // e[i] holds W[d0+i][col0 .. col0+3]; operand j needs W[d0..d0+7][col0+j]
+      e[k][i] = *reinterpret_cast<const u32x2*>(wh + static_cast<int64_t>(d0 + i) * D_C);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load issued before the first wait
+  floatx16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = floatx16{};
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    // e[k][i] holds W[d0+i][col0 .. col0+3]; operand j needs W[d0..d0+7][col0+j]
     u32x4 bj[4];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      bj[0][k] = lo_lo(e[2 * k][0], e[2 * k + 1][0]);
-      bj[1][k] = hi_hi(e[2 * k][0], e[2 * k + 1][0]);
-      bj[2][k] = lo_lo(e[2 * k][1], e[2 * k + 1][1]);
-      bj[3][k] = hi_hi(e[2 * k][1], e[2 * k + 1][1]);
+    for (int r = 0; r < 4; r++) {
+      bj[0][r] = lo_lo(e[k][2 * r][0], e[k][2 * r + 1][0]);
+      bj[1][r] = hi_hi(e[k][2 * r][0], e[k][2 * r + 1][0]);
+      bj[2][r] = lo_lo(e[k][2 * r][1], e[k][2 * r + 1][1]);
+      bj[3][r] = hi_hi(e[k][2 * r][1], e[k][2 * r + 1][1]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[j] = mfma32x32x16(as_bf16x8(a), as_bf16x8(bj[j]), acc[j]);
+    for (int j = 0; j < 4; j++) acc[j] = mfma32x32x16(as_bf16x8(a[k]), as_bf16x8(bj[j]), acc[j]);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++)
+        red[wave - 1][j][q4][lane] = floatx4{acc[j][4 * q4], acc[j][4 * q4 + 1],
+                                             acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int wv = 0; wv < 3; wv++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const floatx4 v = red[wv][j][q4][lane];
+        acc[j][4 * q4] += v[0];
+        acc[j][4 * q4 + 1] += v[1];
+        acc[j][4 * q4 + 2] += v[2];
+        acc[j][4 * q4 + 3] += v[3];
+      }
   // accumulator r of lane (n, g) is batch row 8*(r/4) + 4*g + r%4, column col0 + j
 #pragma unroll
   for (int r = 0; r < 16; r++) {
@@ -97,8 +129,8 @@ __global__ __launch_bounds__(256) void absorb_q_f32_kernel(const float* __restri
 hipError_t launch_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, int B, int n_h,
                            bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int waves = n_h * 4 * ((B + 31) / 32);
-    hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream,
+    const int blocks = n_h * 4 * ((B + 31) / 32);
+    hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(wkv_b),
                        static_cast<uint16_t*>(q_lat), B, n_h);
   } else {

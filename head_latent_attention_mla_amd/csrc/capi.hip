@@ -176,7 +176,8 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(latent) || !aligned16(rope) ||
       !aligned16(out_lat) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3)))
     return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
-  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "scale must be finite and positive");
   SplitPlan sp;
   if (!plan_splits(B, n_h, rows, sparse, num_splits, &sp))
     return fail(MLA_ERR_INVALID_ARG, "num_splits=%d outside [%d, %d]", num_splits,

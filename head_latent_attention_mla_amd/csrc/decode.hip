@@ -47,26 +47,34 @@ namespace mla {
 
 constexpr int TILE = 32;                          // rows per tile
 constexpr int NWAVES = 8;                         // waves per workgroup
-constexpr int LAT_BYTES = TILE * D_C * 2;         // 32 KiB latent region
+constexpr int LAT_PITCH = 68 * 16;                // bytes per latent row in LDS
+constexpr int LAT_BYTES = TILE * LAT_PITCH;       // 34 KiB latent region
 constexpr int ROPE_BYTES = TILE * D_R * 2;        // 4 KiB rotary region
 constexpr int BUF_BYTES = LAT_BYTES + ROPE_BYTES; // one staged tile
+constexpr int NBUF = 3;                           // tiles in LDS (2 in flight)
 constexpr int MAX_SPARSE_ROWS = 1024;             // staged top-k indices per split
-constexpr int QK_STEPS = D_QK / 16 / 2;           // 18 k-steps per feature half
+constexpr int QK_P_STEPS = 20;                    // latent k-steps of the partner wave
+constexpr int QK_O_STEPS = D_C / 16 - QK_P_STEPS; // latent k-steps of the owner wave
+constexpr int QK_ROPE_STEPS = D_R / 16;           // 4 rotary k-steps (partner wave)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// LDS tile layout: latent rows of 64 16-byte chunks, rotary rows of 8, with
-// the chunk index XOR-swizzled per row (inside aligned groups of 16 and 8
-// chunks). swz_lat is injective on the 16 rows a 16-byte score read serves
-// together ({0..3,16..19,4..7,20..23} and its +8 shift) and gives the 4
-// consecutive rows of a transposing read distinct bank quarters; swz_rope
-// does the same for 128-byte rotary rows (row parity supplies the 4th bit).
-__device__ __forceinline__ int swz_lat(int r) {
-  return ((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
-}
+// LDS tile layout.
+// Latent: row r occupies a 68-chunk (1088-byte) slot and its 64 data chunks
+// start at chunk lat_shift(r) of the slot. With 64 four-byte banks a 16-byte
+// chunk at slot chunk position x of row r lands in bank quarter
+// (4r + x) mod 16, so:
+//   * a 16-byte score read (16 lanes, rows {0..3,16..19,4..7,20..23} or the
+//     +8 set, one chunk) hits 16 distinct quarters, and
+//   * a transposing read (4 consecutive rows x 4 consecutive chunks) does too,
+// while every address stays affine in the tile coordinates (one base register
+// per lane plus instruction immediates).
+// Rotary: rows of 8 chunks, chunk index XOR-swizzled by swz_rope (row parity
+// supplies the 4th bit); only the score reads touch it, one row per lane.
+__device__ __forceinline__ int lat_shift(int r) { return ((r >> 2) & 1) | (((r >> 4) & 1) << 1); }
 __device__ __forceinline__ int swz_rope(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
 }
@@ -129,6 +137,7 @@ __device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t l
                                            int row_end, int row_begin, uint32_t dst, int wave,
                                            int lane) {
   const int valid = row_end - row0;
+  const uint32_t voff = static_cast<uint32_t>(lane * 16);
 #pragma unroll
   for (int k = 0; k < TILE / NWAVES; k++) {
     const int R = NWAVES * k + wave;  // wave-uniform tile row
@@ -138,32 +147,85 @@ __device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t l
       grow = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(idx_lds[row0 - row_begin + Rc]));
     else
       grow = static_cast<uint32_t>(row0 + Rc);
-    dma16(lat_d, dst + R * 1024, static_cast<uint32_t>((lane ^ swz_lat(R)) * 16),
+    dma16(lat_d, dst + R * LAT_PITCH + 16 * lat_shift(R), voff,
           __builtin_amdgcn_readfirstlane(grow * lat_rb));
   }
   if (wave < 4) {
     const int R = 8 * wave + (lane >> 3);
     const int Rc = R < valid ? R : valid - 1;
     const uint32_t c = static_cast<uint32_t>((lane & 7) ^ swz_rope(R));
-    uint32_t voff, soff;
+    uint32_t vo, so;
     if (SPARSE) {
-      voff = static_cast<uint32_t>(idx_lds[row0 - row_begin + Rc]) * rope_rb + c * 16;
-      soff = 0;
+      vo = static_cast<uint32_t>(idx_lds[row0 - row_begin + Rc]) * rope_rb + c * 16;
+      so = 0;
     } else {
-      voff = static_cast<uint32_t>(Rc) * rope_rb + c * 16;
-      soff = static_cast<uint32_t>(row0) * rope_rb;
+      vo = static_cast<uint32_t>(Rc) * rope_rb + c * 16;
+      so = static_cast<uint32_t>(row0) * rope_rb;
     }
-    dma16(rope_d, dst + LAT_BYTES + wave * 1024, voff, __builtin_amdgcn_readfirstlane(soff));
+    dma16(rope_d, dst + LAT_BYTES + wave * 1024, vo, __builtin_amdgcn_readfirstlane(so));
   }
+}
+
+// max / sum of a value over lanes l and l^32 (the two lane halves hold the
+// same head), on the VALU: v_permlane32_swap exchanges the halves.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Partial scores S^T[32 rows x 32 heads] of one wave over its k-steps of a
+// staged tile: NSTEPS latent k-steps from byte offset s_off of the tile
+// (32 bytes per k-step), plus, for the partner (ROPE), the 4 rotary k-steps
+// with query operands from LDS. A operands are read 2 k-steps ahead into
+// distinct registers; sched_barrier keeps (read ahead, multiply) so LDS
+// latency hides behind the MFMAs.
+template <int NSTEPS, bool ROPE>
+__device__ __forceinline__ floatx16 partial_scores(const char* buf, int s_off, const bf16x8* q,
+                                                   const u32x4* qpe_w, int lane) {
+  floatx16 sacc = {};
+  const char* sp = buf + s_off;
+  u32x4 ring[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) ring[j] = *reinterpret_cast<const u32x4*>(sp + 32 * j);
+#pragma unroll
+  for (int j = 0; j < NSTEPS; j++) {
+    const u32x4 a = ring[j % 2];
+    if (j + 2 < NSTEPS) ring[j % 2] = *reinterpret_cast<const u32x4*>(sp + 32 * (j + 2));
+    sacc = mfma32x32x16(as_bf16x8(a), q[j], sacc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (ROPE) {
+    // rotary rows: chunk 2j+g of row pi(n), XOR-swizzled; recomputed here
+    // from an opaque lane id rather than kept live across the tile loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int srow = pi_row(lid & 31);
+    const char* rp = buf + LAT_BYTES + srow * 128;
+    const int r_x = (lid >> 5) ^ swz_rope(srow);
+#pragma unroll
+    for (int j = 0; j < QK_ROPE_STEPS; j++) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(rp + (((2 * j) ^ r_x) << 4));
+      const u32x4 bq = qpe_w[j * 64 + lane];
+      sacc = mfma32x32x16(as_bf16x8(a), as_bf16x8(bq), sacc);
+    }
+  }
+  return sacc;
 }
 
 template <bool SPARSE>
 __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char tiles[2 * BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // kh=0 partial scores
+  __shared__ __attribute__((aligned(16))) char tiles[NBUF * BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // partner partial scores
   __shared__ __attribute__((aligned(16))) u32x4 pb[4 * 2 * 64];   // P operands [hq][kk][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 qpe[4 * 4 * 64];  // rotary query operands
   __shared__ float fac[128];                                       // rescale factor per head
-  __shared__ int flag[4];                                          // head quarter rescaled
+  __shared__ __attribute__((aligned(16))) int flag[4];             // head quarter rescaled
   __shared__ float linv[128];                                      // 1 / sum per head
   __shared__ int idx_lds[SPARSE ? MAX_SPARSE_ROWS : 1];
 
@@ -171,7 +233,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int hq = wave & 3, kh = wave >> 2;  // score role: head quarter, feature half
+  const int hq = wave & 3, kh = wave >> 2;  // score role: head quarter, 0 partner / 1 owner
   const int head = hg * 128 + hq * 32 + n;  // score-role head of this lane
   const int headc = min(head, p.n_h - 1);   // clamped for loads
 
@@ -192,47 +254,24 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     for (int i = threadIdx.x; i < row_end - row_begin; i += NWAVES * 64) idx_lds[i] = src[i];
     __syncthreads();
   }
+  // prologue DMA: tiles 0 and 1
   issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin, row_end, row_begin,
                      tiles_addr, wave, lane);
+  if (ntiles > 1)
+    issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + TILE, row_end,
+                       row_begin, tiles_addr + BUF_BYTES, wave, lane);
 
-  // queries of the score role as MFMA B operands: k-step ks = 18kh + j covers
-  // features 16ks .. 16ks+15 of [q_lat ; q_pe], lane half g the 8 at 16ks + 8g
-  bf16x8 q[QK_STEPS];
-  {
-    const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
-    const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C;
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R;
-#pragma unroll
-    for (int j = 0; j < QK_STEPS; j++) {
-      const int f = 16 * (QK_STEPS * kh + j) + 8 * g;
-      q[j] = as_bf16x8(f < D_C ? ld16(ql + f) : ld16(qp + (f - D_C)));
-    }
-  }
-
-  // score-read offsets: chunk 2ks+g of tile row pi(n); the swizzle only
-  // touches the low chunk bits
+  // per-lane LDS byte offsets inside a tile buffer (tile-independent)
   const int srow = pi_row(n);
-  const int s_lat = srow * 1024;
-  const int s_lat_x = g ^ swz_lat(srow);
-  const int s_rope = LAT_BYTES + srow * 128;
-  const int s_rope_x = g ^ swz_rope(srow);
-  // transposing-read offsets of the mix: feature tile dt = 2*wave + mt,
-  // lane supplies tile row 16g + 8kk + 4rd + (lane%16)/4
-  int pv_off[2][2][2];
+  const int s_off = srow * LAT_PITCH + 16 * (lat_shift(srow) + g) + 32 * QK_P_STEPS * kh;
+  int m_off;  // transposing reads: + 8704kk + 4368rd + 64mt
   {
     const int tau = tau_blk(4 * ((lane >> 4) & 1) + (lane & 3));
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-      for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-        for (int rd = 0; rd < 2; rd++) {
-          const int dt = 2 * wave + mt;
-          const int row = 16 * g + 8 * kk + 4 * rd + ((lane & 15) >> 2);
-          pv_off[mt][kk][rd] = row * 1024 + 16 * ((4 * (dt & 3) + (tau >> 1)) ^ swz_lat(row)) +
-                               8 * (tau & 1) + 256 * (dt >> 2);
-        }
+    const int row0 = 16 * g + ((lane & 15) >> 2);
+    m_off = row0 * LAT_PITCH + 16 * (2 * g + (tau >> 1)) + 8 * (tau & 1) + 64 * 2 * wave;
   }
+  const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
+  const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
 
   floatx16 acc[2][4];  // mix accumulators [feature tile][head tile]
 #pragma unroll
@@ -244,12 +283,21 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const float sl2 = p.scale * LOG2E;
   const int my_loads = TILE / NWAVES + (wave < 4 ? 1 : 0);
 
-  for (int it = 0; it < ntiles; it++) {
-    const int row0 = row_begin + it * TILE;
-    const char* buf = tiles + (it & 1) * BUF_BYTES;
-    if (it + 1 < ntiles) {
-      issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row0 + TILE, row_end,
-                         row_begin, tiles_addr + ((it + 1) & 1) * BUF_BYTES, wave, lane);
+  // ---- software-pipelined tile loop ---------------------------------------------
+  // Entering iteration it: the owner waves hold the complete scores S of tile
+  // it; tile it and (if any) tile it+1 are in LDS or in flight. Per iteration:
+  //   barrier A   tile it+1 resident, mix of tile it-1 done (its buffer is
+  //               refilled with tile it+2)
+  //   phase 1     owner: softmax(it) -> P, rescale factors
+  //               partner: partial scores of tile it+1 -> LDS
+  //   barrier B
+  //   phase 2     everyone: mix(it); owner: own partial scores of tile it+1
+  //               plus the partner's -> S
+  // The two roles run separate copies of the prologue and loop (kh is
+  // wave-uniform) with their own query registers; both pass the same
+  // barriers in the same order.
+  auto tile0_wait = [&]() {
+    if (ntiles > 1) {
       if (my_loads == 5)
         asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
       else
@@ -257,53 +305,120 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();  // tile `it` is in LDS; the previous tile's mix is done
-
-    // ---- partial scores over this wave's feature half ------------------------
-    floatx16 sacc = {};
-    {
-      auto score_a = [&](int ks) -> u32x4 {
-        if (ks < D_C / 16)
-          return *reinterpret_cast<const u32x4*>(buf + s_lat + (((2 * (ks & 7)) ^ s_lat_x) << 4) +
-                                                 256 * (ks >> 3));
-        return *reinterpret_cast<const u32x4*>(buf + s_rope +
-                                               (((2 * (ks - D_C / 16)) ^ s_rope_x) << 4));
-      };
-      if (kh == 0) {
+    __syncthreads();  // tile 0 resident; rotary queries staged
+  };
+  auto top_of_tile = [&](int it) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile it+1 resident
+    __syncthreads();
+    if (it + 2 < ntiles)  // refill the buffer of tile it-1 with tile it+2
+      issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + (it + 2) * TILE,
+                         row_end, row_begin, tiles_addr + ((it + 2) % NBUF) * BUF_BYTES, wave,
+                         lane);
+  };
+  auto mix = [&](const char* buf) {
+    const i32x4 fl = *reinterpret_cast<const i32x4*>(flag);
+    if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
-        for (int j = 0; j < QK_STEPS; j++) sacc = mfma32x32x16(as_bf16x8(score_a(j)), q[j], sacc);
-      } else {
-#pragma unroll
-        for (int j = 0; j < QK_STEPS; j++)
-          sacc = mfma32x32x16(as_bf16x8(score_a(QK_STEPS + j)), q[j], sacc);
-      }
-    }
-    if (kh == 0) {
-      float4* dstx = reinterpret_cast<float4*>(sx) + hq * 256 + lane;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++)
-        dstx[64 * j4] = make_float4(sacc[4 * j4], sacc[4 * j4 + 1], sacc[4 * j4 + 2], sacc[4 * j4 + 3]);
-    }
-    __syncthreads();  // partial scores published
-
-    // ---- online softmax (owner waves, log2 domain) -----------------------------
-    if (kh == 1) {
-      const float4* srcx = reinterpret_cast<const float4*>(sx) + hq * 256 + lane;
-      const int valid = row_end - row0;  // rows of this tile that exist
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++) {
-        const float4 o = srcx[64 * j4];
-        const float other[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int r = 4 * j4 + i;
-          const float t = (sacc[r] + other[i]) * sl2;
-          sacc[r] = (16 * g + r < valid) ? t : -INFINITY;
-          tmax = fmaxf(tmax, sacc[r]);
+      for (int nt = 0; nt < 4; nt++) {
+        if (fl[nt]) {
+          const float fn = fac[nt * 32 + n];
+          acc[0][nt] *= fn;
+          acc[1][nt] *= fn;
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // lanes n and n+32 share a head
+    }
+    const char* mp = buf + m_off;
+    bf16x8 A[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+        A[mt][kk] = tr_pair(mp + 8704 * kk + 64 * mt, mp + 8704 * kk + 4368 + 64 * mt);
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+      const bf16x8 B0 = as_bf16x8(pb[(nt * 2 + 0) * 64 + lane]);
+      const bf16x8 B1 = as_bf16x8(pb[(nt * 2 + 1) * 64 + lane]);
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        acc[mt][nt] = mfma32x32x16(A[mt][0], B0, acc[mt][nt]);
+        acc[mt][nt] = mfma32x32x16(A[mt][1], B1, acc[mt][nt]);
+      }
+    }
+  };
+  float4* const sx_w = reinterpret_cast<float4*>(sx) + hq * 256 + lane;
+
+  if (kh == 0) {
+    // ======== partner waves: latent k-steps 0..19 and the rotary k-steps ========
+    // query operands: k-step ks covers features 16ks..16ks+15, lane half g the
+    // 8 at 16ks + 8g; rotary operands staged in LDS as [hq][k-step][lane]
+    bf16x8 q[QK_P_STEPS];
+#pragma unroll
+    for (int j = 0; j < QK_P_STEPS; j++) q[j] = as_bf16x8(ld16(ql + 16 * j));
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R + 8 * g;
+#pragma unroll
+      for (int j = 0; j < QK_ROPE_STEPS; j++) qpe[(hq * 4 + j) * 64 + lane] = ld16(qp + 16 * j);
+    }
+    // consume the loads here so the compiler's vmcnt waits stay out of the
+    // tile loop (where they would also wait on tile DMA)
+#pragma unroll
+    for (int j = 0; j < QK_P_STEPS; j++) asm volatile("" : : "v"(q[j]));
+    const u32x4* qpe_w = qpe + hq * 4 * 64;
+
+    tile0_wait();
+    {
+      const floatx16 Sp = partial_scores<QK_P_STEPS, true>(tiles, s_off, q, qpe_w, lane);
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++)
+        sx_w[64 * j4] = make_float4(Sp[4 * j4], Sp[4 * j4 + 1], Sp[4 * j4 + 2], Sp[4 * j4 + 3]);
+    }
+    __syncthreads();  // partner scores of tile 0 published
+    for (int it = 0; it < ntiles; it++) {
+      top_of_tile(it);
+      if (it + 1 < ntiles) {
+        const floatx16 Sp = partial_scores<QK_P_STEPS, true>(
+            tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q, qpe_w, lane);
+#pragma unroll
+        for (int j4 = 0; j4 < 4; j4++)
+          sx_w[64 * j4] = make_float4(Sp[4 * j4], Sp[4 * j4 + 1], Sp[4 * j4 + 2], Sp[4 * j4 + 3]);
+      }
+      __syncthreads();  // barrier B
+      mix(tiles + (it % NBUF) * BUF_BYTES);
+    }
+  } else {
+    // ======== owner waves: latent k-steps 20..31 and the softmax ========
+    bf16x8 q[QK_O_STEPS];
+#pragma unroll
+    for (int j = 0; j < QK_O_STEPS; j++) q[j] = as_bf16x8(ld16(ql + 16 * (QK_P_STEPS + j)));
+#pragma unroll
+    for (int j = 0; j < QK_O_STEPS; j++) asm volatile("" : : "v"(q[j]));
+
+    tile0_wait();
+    floatx16 S = partial_scores<QK_O_STEPS, false>(tiles, s_off, q, nullptr, lane);
+    __syncthreads();  // partner scores of tile 0 published
+#pragma unroll
+    for (int j4 = 0; j4 < 4; j4++) {
+      const float4 o = sx_w[64 * j4];
+      S[4 * j4] += o.x;
+      S[4 * j4 + 1] += o.y;
+      S[4 * j4 + 2] += o.z;
+      S[4 * j4 + 3] += o.w;
+    }
+    for (int it = 0; it < ntiles; it++) {
+      top_of_tile(it);
+      const int row0 = row_begin + it * TILE;
+      // ---- phase 1: online softmax of tile it (log2 domain) ----
+      const int valid = row_end - row0;  // rows of this tile that exist
+      if (valid < TILE) {
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (16 * g + r >= valid) S[r] = -INFINITY;
+      }
+      float smax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; r++) smax = fmaxf(smax, S[r]);
+      // scale > 0, so the max of the scaled scores is the scaled max
+      const float tmax = pair_max(smax * sl2);
       int rescaled = 0;
       float f = 1.f;
       if (__any(tmax > m + RESCALE_SLACK)) {
@@ -313,13 +428,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
         m = m_new;
         rescaled = 1;
       }
+      const float nm = -m;
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 P;
 #pragma unroll
         for (int w2 = 0; w2 < 4; w2++) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[8 * kk + 2 * w2] - m);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[8 * kk + 2 * w2 + 1] - m);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * kk + 2 * w2], sl2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * kk + 2 * w2 + 1], sl2, nm));
           P[w2] = pack_bf16x2(p0, p1);
           // the denominator sums the rounded weights the mix actually uses
           l += __uint_as_float(P[w2] << 16) + __uint_as_float(P[w2] & 0xFFFF0000u);
@@ -328,33 +444,19 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       }
       if (g == 0) fac[hq * 32 + n] = f;
       if (lane == 0) flag[hq] = rescaled;
-    }
-    __syncthreads();  // P and rescale factors published
-
-    // ---- probability-weighted latent: features 64w..64w+63, all heads --------
-    {
+      __syncthreads();  // barrier B
+      // ---- phase 2 ----
+      mix(tiles + (it % NBUF) * BUF_BYTES);
+      if (it + 1 < ntiles) {
+        S = partial_scores<QK_O_STEPS, false>(tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q,
+                                              nullptr, lane);
 #pragma unroll
-      for (int nt = 0; nt < 4; nt++) {
-        if (flag[nt]) {
-          const float fn = fac[nt * 32 + n];
-          acc[0][nt] *= fn;
-          acc[1][nt] *= fn;
-        }
-      }
-      bf16x8 A[2][2];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-          A[mt][kk] = tr_pair(buf + pv_off[mt][kk][0], buf + pv_off[mt][kk][1]);
-#pragma unroll
-      for (int nt = 0; nt < 4; nt++) {
-        const bf16x8 B0 = as_bf16x8(pb[(nt * 2 + 0) * 64 + lane]);
-        const bf16x8 B1 = as_bf16x8(pb[(nt * 2 + 1) * 64 + lane]);
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
-          acc[mt][nt] = mfma32x32x16(A[mt][0], B0, acc[mt][nt]);
-          acc[mt][nt] = mfma32x32x16(A[mt][1], B1, acc[mt][nt]);
+        for (int j4 = 0; j4 < 4; j4++) {
+          const float4 o = sx_w[64 * j4];
+          S[4 * j4] += o.x;
+          S[4 * j4 + 1] += o.y;
+          S[4 * j4 + 2] += o.z;
+          S[4 * j4 + 3] += o.w;
         }
       }
     }
@@ -363,7 +465,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   // ---- epilogue -----------------------------------------------------------------
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
   if (kh == 1) {
-    const float l_tot = l + __shfl_xor(l, 32);
+    const float l_tot = pair_sum(l);
     if (g == 0) linv[hq * 32 + n] = 1.f / l_tot;
     if (g == 0 && head < p.n_h) {
       const float lse_v = (m + log2f(l_tot)) * LN2;  // natural log of sum exp(z)

@@ -8,9 +8,11 @@
 //
 // Per head a [B x 512] x [512 x 128] product bound by streaming the 16 MiB of
 // W^UV. Here the contraction runs along W's contiguous axis, so both MFMA
-// operands are straight 16-byte loads: one wave per (head, 32-wide value
-// tile, 32-row batch tile), v_mfma_f32_32x32x16_bf16 with M = batch rows,
-// N = value features, K = latent features.
+// operands are straight 16-byte loads. One workgroup of 4 waves per (head,
+// 32-wide value tile, 32-row batch tile); wave w takes latent features
+// [128w, 128w+128) (8 k-steps of v_mfma_f32_32x32x16_bf16 with M = batch
+// rows, N = value features) and issues all 16 of its loads before the first
+// multiply; the four partial sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,35 +22,53 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ w,
                                                           uint16_t* __restrict__ out, int B,
                                                           int n_h) {
-  const int lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) floatx4 red[3][4][64];  // waves 1..3 partials
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
   const int nbt = (B + 31) >> 5;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gw >= n_h * 4 * nbt) return;
-  const int bt = gw % nbt;
-  const int dt = (gw / nbt) & 3;
-  const int h = gw / (nbt * 4);
-  const int b = bt * 32 + n;
+  const int bt = blockIdx.x % nbt;
+  const int dt = (blockIdx.x / nbt) & 3;
+  const int h = blockIdx.x / (nbt * 4);
+  // rows past B load row B-1 (unconditional loads keep all 16 in flight);
+  // their results are never stored
+  const int b = min(bt * 32 + n, B - 1);
   const int d = dt * 32 + n;  // this lane's B-operand column (value feature)
-  const uint16_t* orow = o_lat + (static_cast<int64_t>(b) * n_h + h) * D_C;
-  const uint16_t* wrow = w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C;
+  const uint16_t* orow = o_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + wave * 128 + g * 8;
+  const uint16_t* wrow =
+      w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C + wave * 128 + g * 8;
 
-  floatx16 acc0 = {}, acc1 = {};
-#pragma unroll 4
-  for (int ks = 0; ks < D_C / 16; ks += 2) {
-    const int c0 = ks * 16 + g * 8;
-    u32x4 a0 = (b < B) ? ld16(orow + c0) : u32x4{0, 0, 0, 0};
-    u32x4 a1 = (b < B) ? ld16(orow + c0 + 16) : u32x4{0, 0, 0, 0};
-    u32x4 w0 = ld16(wrow + c0);
-    u32x4 w1 = ld16(wrow + c0 + 16);
-    acc0 = mfma32x32x16(as_bf16x8(a0), as_bf16x8(w0), acc0);
-    acc1 = mfma32x32x16(as_bf16x8(a1), as_bf16x8(w1), acc1);
+  u32x4 a[8], bw[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    a[k] = ld16(orow + 16 * k);
+    bw[k] = ld16(wrow + 16 * k);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load issued before the first wait
+  floatx16 acc = {};
+#pragma unroll
+  for (int k = 0; k < 8; k++) acc = mfma32x32x16(as_bf16x8(a[k]), as_bf16x8(bw[k]), acc);
+  if (wave > 0) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++)
+      red[wave - 1][q4][lane] =
+          floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int wv = 0; wv < 3; wv++)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const floatx4 v = red[wv][q4][lane];
+      acc[4 * q4] += v[0];
+      acc[4 * q4 + 1] += v[1];
+      acc[4 * q4 + 2] += v[2];
+      acc[4 * q4 + 3] += v[3];
+    }
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int bo = bt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (bo < B)
-      out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(acc0[r] + acc1[r]);
+    if (bo < B) out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(acc[r]);
   }
 }
 
@@ -71,8 +91,8 @@ __global__ __launch_bounds__(128) void out_up_f32_kernel(const float* __restrict
 hipError_t launch_out_up(const void* o_lat, const void* wkv_b, void* out, int B, int n_h,
                          bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int waves = n_h * 4 * ((B + 31) / 32);
-    hipLaunchKernelGGL(out_up_bf16_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream,
+    const int blocks = n_h * 4 * ((B + 31) / 32);
+    hipLaunchKernelGGL(out_up_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(wkv_b),
                        static_cast<uint16_t*>(out), B, n_h);
   } else {
