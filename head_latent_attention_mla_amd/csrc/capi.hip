@@ -2,6 +2,7 @@
 // argument checks, split planning for the decode call, and kernel dispatch.
 // Every check happens before the first HIP call; the library never
 // allocates, frees or synchronises.
+#include <climits>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -176,6 +177,10 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(latent) || !aligned16(rope) ||
       !aligned16(out_lat) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3)))
     return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  // bf16 rows are fetched with 32-bit byte offsets from each sequence's base
+  if (dt == MLA_BF16 && (static_cast<int64_t>(T) * lat_rstride * 2 > INT32_MAX ||
+                         static_cast<int64_t>(T) * rope_rstride * 2 > INT32_MAX))
+    return fail(MLA_ERR_UNSUPPORTED, "T * row stride above 2^31 bytes");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "scale must be finite and positive");
   SplitPlan sp;
@@ -184,6 +189,10 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
                 sparse ? ((rows + 31) / 32 + kMaxSparseTilesPerSplit - 1) / kMaxSparseTilesPerSplit
                        : 1,
                 (rows + 31) / 32);
+  if (static_cast<int64_t>(sp.num_splits) * ((n_h + 127) / 128) * B > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 workgroups");
+  if (sp.num_splits > 1 && static_cast<int64_t>(B) * n_h > (int64_t{1} << 26))
+    return fail(MLA_ERR_UNSUPPORTED, "B * n_h above 2^26 with split rows");
   const size_t need = ws_bytes_for(B, n_h, sp, dt);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

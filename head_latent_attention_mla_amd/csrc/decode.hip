@@ -53,9 +53,17 @@ constexpr int ROPE_BYTES = TILE * D_R * 2;        // 4 KiB rotary region
 constexpr int BUF_BYTES = LAT_BYTES + ROPE_BYTES; // one staged tile
 constexpr int NBUF = 3;                           // tiles in LDS (2 in flight)
 constexpr int MAX_SPARSE_ROWS = 1024;             // staged top-k indices per split
-constexpr int QK_P_STEPS = 20;                    // latent k-steps of the partner wave
+constexpr int QK_P_STEPS = 19;                    // latent k-steps of the partner wave
 constexpr int QK_O_STEPS = D_C / 16 - QK_P_STEPS; // latent k-steps of the owner wave
 constexpr int QK_ROPE_STEPS = D_R / 16;           // 4 rotary k-steps (partner wave)
+#ifndef MLA_P_RING
+#define MLA_P_RING 2
+#endif
+#ifndef MLA_O_RING
+#define MLA_O_RING 2
+#endif
+constexpr int P_RING = MLA_P_RING;  // tile-operand read-ahead of the partner's k-steps
+constexpr int O_RING = MLA_O_RING;  // and of the owner's
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
@@ -126,32 +134,30 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Stage rows [row0, row0+32) of this split into the LDS tile at byte address
-// `dst` (rows at or beyond row_end re-read row row_end-1; their
-// probabilities are zero). Latent: 4 instructions per wave, each one tile
-// row of 64 chunks (the row's global offset is a scalar). Rotary: waves 0..3
-// load 8 rows x 8 chunks each.
-template <bool SPARSE>
-__device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t lat_rb,
+// Staging of rows [row0, row0+32) of this split into the LDS tile at byte
+// address `dst` by NW waves (w = 0..NW-1), one instruction per call: step
+// k < 32/NW stages latent row NW*k + w (64 chunks of 16 bytes; the row's
+// global offset is a scalar); step 32/NW stages the rotary rows 8w..8w+7
+// (waves w < 4). Rows at or beyond row_end re-read row row_end-1 (their
+// probabilities are zero).
+template <bool SPARSE, int NW>
+__device__ __forceinline__ void stage_step(int k, i32x4 lat_d, i32x4 rope_d, uint32_t lat_rb,
                                            uint32_t rope_rb, const int* idx_lds, int row0,
-                                           int row_end, int row_begin, uint32_t dst, int wave,
+                                           int row_end, int row_begin, uint32_t dst, int w,
                                            int lane) {
   const int valid = row_end - row0;
-  const uint32_t voff = static_cast<uint32_t>(lane * 16);
-#pragma unroll
-  for (int k = 0; k < TILE / NWAVES; k++) {
-    const int R = NWAVES * k + wave;  // wave-uniform tile row
+  if (k < TILE / NW) {
+    const int R = NW * k + w;  // wave-uniform tile row
     const int Rc = R < valid ? R : valid - 1;
     uint32_t grow;
     if (SPARSE)
       grow = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(idx_lds[row0 - row_begin + Rc]));
     else
       grow = static_cast<uint32_t>(row0 + Rc);
-    dma16(lat_d, dst + R * LAT_PITCH + 16 * lat_shift(R), voff,
+    dma16(lat_d, dst + R * LAT_PITCH + 16 * lat_shift(R), static_cast<uint32_t>(lane * 16),
           __builtin_amdgcn_readfirstlane(grow * lat_rb));
-  }
-  if (wave < 4) {
-    const int R = 8 * wave + (lane >> 3);
+  } else if (w < 4) {
+    const int R = 8 * w + (lane >> 3);
     const int Rc = R < valid ? R : valid - 1;
     const uint32_t c = static_cast<uint32_t>((lane & 7) ^ swz_rope(R));
     uint32_t vo, so;
@@ -162,8 +168,20 @@ __device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t l
       vo = static_cast<uint32_t>(Rc) * rope_rb + c * 16;
       so = static_cast<uint32_t>(row0) * rope_rb;
     }
-    dma16(rope_d, dst + LAT_BYTES + wave * 1024, vo, __builtin_amdgcn_readfirstlane(so));
+    dma16(rope_d, dst + LAT_BYTES + w * 1024, vo, __builtin_amdgcn_readfirstlane(so));
   }
+}
+
+// The whole staging of a tile by all NWAVES waves (prologue).
+template <bool SPARSE>
+__device__ __forceinline__ void issue_tile(i32x4 lat_d, i32x4 rope_d, uint32_t lat_rb,
+                                           uint32_t rope_rb, const int* idx_lds, int row0,
+                                           int row_end, int row_begin, uint32_t dst, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int k = 0; k <= TILE / NWAVES; k++)
+    stage_step<SPARSE, NWAVES>(k, lat_d, rope_d, lat_rb, rope_rb, idx_lds, row0, row_end,
+                               row_begin, dst, wave, lane);
 }
 
 // max / sum of a value over lanes l and l^32 (the two lane halves hold the
@@ -180,40 +198,47 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 // Partial scores S^T[32 rows x 32 heads] of one wave over its k-steps of a
-// staged tile: NSTEPS latent k-steps from byte offset s_off of the tile
-// (32 bytes per k-step), plus, for the partner (ROPE), the 4 rotary k-steps
-// with query operands from LDS. A operands are read 2 k-steps ahead into
-// distinct registers; sched_barrier keeps (read ahead, multiply) so LDS
-// latency hides behind the MFMAs.
-template <int NSTEPS, bool ROPE>
+// staged tile: NL latent k-steps from byte offset s_off of the tile (32 bytes
+// per k-step), then, for the partner (ROPE), the 4 rotary k-steps. Query
+// operands q[] are registers, the rotary ones (qpe_w) LDS. Tile operands are read RING k-steps ahead into
+// distinct registers (an LDS round trip is several MFMA durations). With
+// PINNED, sched_barrier keeps each (read ahead, multiply) pair in place;
+// without, the scheduler may interleave other independent work (the owner's
+// softmax) between them. hook(j) runs before multiply j (the owner issues
+// its share of the tile DMA there).
+template <int NL, bool ROPE, int RING, bool PINNED, class Hook>
 __device__ __forceinline__ floatx16 partial_scores(const char* buf, int s_off, const bf16x8* q,
-                                                   const u32x4* qpe_w, int lane) {
+                                                   const u32x4* qpe_w, int lane, Hook&& hook) {
+  constexpr int N = NL + (ROPE ? QK_ROPE_STEPS : 0);
   floatx16 sacc = {};
   const char* sp = buf + s_off;
-  u32x4 ring[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) ring[j] = *reinterpret_cast<const u32x4*>(sp + 32 * j);
-#pragma unroll
-  for (int j = 0; j < NSTEPS; j++) {
-    const u32x4 a = ring[j % 2];
-    if (j + 2 < NSTEPS) ring[j % 2] = *reinterpret_cast<const u32x4*>(sp + 32 * (j + 2));
-    sacc = mfma32x32x16(as_bf16x8(a), q[j], sacc);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  // rotary rows: chunk 2j+g of row pi(n), XOR-swizzled; recomputed here from
+  // an opaque lane id rather than kept live across the tile loop
+  const char* rp = buf;
+  int r_x = 0;
   if (ROPE) {
-    // rotary rows: chunk 2j+g of row pi(n), XOR-swizzled; recomputed here
-    // from an opaque lane id rather than kept live across the tile loop
     int lid = lane;
     asm volatile("" : "+v"(lid));
     const int srow = pi_row(lid & 31);
-    const char* rp = buf + LAT_BYTES + srow * 128;
-    const int r_x = (lid >> 5) ^ swz_rope(srow);
+    rp = buf + LAT_BYTES + srow * 128;
+    r_x = (lid >> 5) ^ swz_rope(srow);
+  }
+  auto operand = [&](int j) -> u32x4 {
+    if (j < NL) return *reinterpret_cast<const u32x4*>(sp + 32 * j);
+    return *reinterpret_cast<const u32x4*>(rp + (((2 * (j - NL)) ^ r_x) << 4));
+  };
+  u32x4 ring[RING];
 #pragma unroll
-    for (int j = 0; j < QK_ROPE_STEPS; j++) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(rp + (((2 * j) ^ r_x) << 4));
-      const u32x4 bq = qpe_w[j * 64 + lane];
-      sacc = mfma32x32x16(as_bf16x8(a), as_bf16x8(bq), sacc);
-    }
+  for (int j = 0; j < RING; j++) ring[j] = operand(j);
+#pragma unroll
+  for (int j = 0; j < N; j++) {
+    const u32x4 a = ring[j % RING];
+    if (j + RING < N) ring[j % RING] = operand(j + RING);
+    // rotary query operands come from LDS (registers are full)
+    const bf16x8 b = j < NL ? q[j] : as_bf16x8(qpe_w[(j - NL) * 64 + lane]);
+    hook(j);
+    sacc = mfma32x32x16(as_bf16x8(a), b, sacc);
+    if (PINNED) __builtin_amdgcn_sched_barrier(0);
   }
   return sacc;
 }
@@ -222,14 +247,26 @@ template <bool SPARSE>
 __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char tiles[NBUF * BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // partner partial scores
-  __shared__ __attribute__((aligned(16))) u32x4 pb[4 * 2 * 64];   // P operands [hq][kk][lane]
   __shared__ __attribute__((aligned(16))) u32x4 qpe[4 * 4 * 64];  // rotary query operands
+  __shared__ __attribute__((aligned(16))) u32x4 pb[4 * 2 * 64];   // P operands [hq][kk][lane]
   __shared__ float fac[128];                                       // rescale factor per head
   __shared__ __attribute__((aligned(16))) int flag[4];             // head quarter rescaled
   __shared__ float linv[128];                                      // 1 / sum per head
   __shared__ int idx_lds[SPARSE ? MAX_SPARSE_ROWS : 1];
 
-  const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order. Renumber
+  // them so that the splits of one (sequence, head group) run on one XCD and
+  // share its L2: the query rows they all read are then fetched once.
+  int s, hg, b;
+  {
+    const int S = gridDim.x, HG = gridDim.y;
+    const int G = S * HG * gridDim.z;
+    const int L = blockIdx.x + S * (blockIdx.y + HG * blockIdx.z);
+    const int j = (G & 7) == 0 ? (L & 7) * (G >> 3) + (L >> 3) : L;
+    s = j % S;
+    hg = (j / S) % HG;
+    b = j / (S * HG);
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
@@ -254,12 +291,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     for (int i = threadIdx.x; i < row_end - row_begin; i += NWAVES * 64) idx_lds[i] = src[i];
     __syncthreads();
   }
-  // prologue DMA: tiles 0 and 1
+  // prologue DMA of tile 0; the query loads that follow are waited for
+  // (by the compiler) before the rest of the prologue DMA is issued
   issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin, row_end, row_begin,
                      tiles_addr, wave, lane);
-  if (ntiles > 1)
-    issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + TILE, row_end,
-                       row_begin, tiles_addr + BUF_BYTES, wave, lane);
 
   // per-lane LDS byte offsets inside a tile buffer (tile-independent)
   const int srow = pi_row(n);
@@ -281,39 +316,43 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   float m = -INFINITY;  // owner waves: running max of scale*log2(e)*score
   float l = 0.f;        // owner waves: this lane's share of the running sum
   const float sl2 = p.scale * LOG2E;
-  const int my_loads = TILE / NWAVES + (wave < 4 ? 1 : 0);
 
   // ---- software-pipelined tile loop ---------------------------------------------
   // Entering iteration it: the owner waves hold the complete scores S of tile
   // it; tile it and (if any) tile it+1 are in LDS or in flight. Per iteration:
-  //   barrier A   tile it+1 resident, mix of tile it-1 done (its buffer is
-  //               refilled with tile it+2)
-  //   phase 1     owner: softmax(it) -> P, rescale factors
+  //   barrier A   tile it+1 resident, mix of tile it-1 done
+  //   phase 1     owner: softmax(it) -> P, rescale factors; then its own
+  //               partial scores of tile it+1 (registers), issuing between
+  //               those multiplies the DMA of tile it+2 into tile it-1's buffer
   //               partner: partial scores of tile it+1 -> LDS
   //   barrier B
-  //   phase 2     everyone: mix(it); owner: own partial scores of tile it+1
-  //               plus the partner's -> S
+  //   phase 2     everyone: mix(it); owner: S of tile it+1 = own partial
+  //               scores plus the partner's
   // The two roles run separate copies of the prologue and loop (kh is
   // wave-uniform) with their own query registers; both pass the same
   // barriers in the same order.
+  // After the query registers have arrived (and with them tile 0): DMA of
+  // tile 1 by all waves, then the barrier that publishes tile 0 (and the
+  // staged rotary queries). In the loop only the owner waves stage tiles.
   auto tile0_wait = [&]() {
-    if (ntiles > 1) {
-      if (my_loads == 5)
-        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else {
+    if (ntiles > 1)
+      issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + TILE, row_end,
+                         row_begin, tiles_addr + BUF_BYTES, wave, lane);
+    // tile 0 resident (in practice already waited for with the queries)
+    if (ntiles == 1)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();  // tile 0 resident; rotary queries staged
-  };
-  auto top_of_tile = [&](int it) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile it+1 resident
+    else if (kh == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(TILE / NWAVES) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(TILE / NWAVES + 1) : "memory");
     __syncthreads();
-    if (it + 2 < ntiles)  // refill the buffer of tile it-1 with tile it+2
-      issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + (it + 2) * TILE,
-                         row_end, row_begin, tiles_addr + ((it + 2) % NBUF) * BUF_BYTES, wave,
-                         lane);
+  };
+  // Top of iteration it: tile it+1 resident (staged by the owners during
+  // iteration it-1, or by everyone in the prologue) and every wave done with
+  // tile it-1.
+  auto top_of_tile = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
   auto mix = [&](const char* buf) {
     const i32x4 fl = *reinterpret_cast<const i32x4*>(flag);
@@ -348,7 +387,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   float4* const sx_w = reinterpret_cast<float4*>(sx) + hq * 256 + lane;
 
   if (kh == 0) {
-    // ======== partner waves: latent k-steps 0..19 and the rotary k-steps ========
+    // ======== partner waves: the first QK_P_STEPS latent k-steps and the rotary ones ==
     // query operands: k-step ks covers features 16ks..16ks+15, lane half g the
     // 8 at 16ks + 8g; rotary operands staged in LDS as [hq][k-step][lane]
     bf16x8 q[QK_P_STEPS];
@@ -367,17 +406,18 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
 
     tile0_wait();
     {
-      const floatx16 Sp = partial_scores<QK_P_STEPS, true>(tiles, s_off, q, qpe_w, lane);
+      const floatx16 Sp = partial_scores<QK_P_STEPS, true, P_RING, true>(tiles, s_off, q, qpe_w, lane,
+                                                                         [](int) {});
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++)
         sx_w[64 * j4] = make_float4(Sp[4 * j4], Sp[4 * j4 + 1], Sp[4 * j4 + 2], Sp[4 * j4 + 3]);
     }
     __syncthreads();  // partner scores of tile 0 published
     for (int it = 0; it < ntiles; it++) {
-      top_of_tile(it);
+      top_of_tile();
       if (it + 1 < ntiles) {
-        const floatx16 Sp = partial_scores<QK_P_STEPS, true>(
-            tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q, qpe_w, lane);
+        const floatx16 Sp = partial_scores<QK_P_STEPS, true, P_RING, true>(
+            tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q, qpe_w, lane, [](int) {});
 #pragma unroll
         for (int j4 = 0; j4 < 4; j4++)
           sx_w[64 * j4] = make_float4(Sp[4 * j4], Sp[4 * j4 + 1], Sp[4 * j4 + 2], Sp[4 * j4 + 3]);
@@ -386,7 +426,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       mix(tiles + (it % NBUF) * BUF_BYTES);
     }
   } else {
-    // ======== owner waves: latent k-steps 20..31 and the softmax ========
+    // ======== owner waves: the last QK_O_STEPS latent k-steps and the softmax ========
     bf16x8 q[QK_O_STEPS];
 #pragma unroll
     for (int j = 0; j < QK_O_STEPS; j++) q[j] = as_bf16x8(ld16(ql + 16 * (QK_P_STEPS + j)));
@@ -394,7 +434,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     for (int j = 0; j < QK_O_STEPS; j++) asm volatile("" : : "v"(q[j]));
 
     tile0_wait();
-    floatx16 S = partial_scores<QK_O_STEPS, false>(tiles, s_off, q, nullptr, lane);
+    floatx16 S = partial_scores<QK_O_STEPS, false, O_RING, true>(tiles, s_off, q, nullptr, lane,
+                                                                  [](int) {});
     __syncthreads();  // partner scores of tile 0 published
 #pragma unroll
     for (int j4 = 0; j4 < 4; j4++) {
@@ -405,29 +446,24 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       S[4 * j4 + 3] += o.w;
     }
     for (int it = 0; it < ntiles; it++) {
-      top_of_tile(it);
-      const int row0 = row_begin + it * TILE;
-      // ---- phase 1: online softmax of tile it (log2 domain) ----
-      const int valid = row_end - row0;  // rows of this tile that exist
-      if (valid < TILE) {
+      top_of_tile();
+      // ---- phase 1: online softmax of tile it (log2 domain), then the own
+      // partial scores of tile it+1 (on the last tile they read a stale
+      // buffer and are discarded); the partner's multiplies fill the
+      // SIMD's MFMA pipe meanwhile ----
+      const int valid = row_end - (row_begin + it * TILE);  // rows of this tile that exist
 #pragma unroll
-        for (int r = 0; r < 16; r++)
-          if (16 * g + r >= valid) S[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
       float smax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r++) smax = fmaxf(smax, S[r]);
       // scale > 0, so the max of the scaled scores is the scaled max
       const float tmax = pair_max(smax * sl2);
-      int rescaled = 0;
-      float f = 1.f;
-      if (__any(tmax > m + RESCALE_SLACK)) {
-        const float m_new = fmaxf(m, tmax);
-        f = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
-        l *= f;
-        m = m_new;
-        rescaled = 1;
-      }
+      const bool rescaled = __any(tmax > m + RESCALE_SLACK);
+      const float m_new = rescaled ? fmaxf(m, tmax) : m;
+      const float f = rescaled ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 on the first tile
+      l *= f;
+      m = m_new;
       const float nm = -m;
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
@@ -444,20 +480,40 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       }
       if (g == 0) fac[hq * 32 + n] = f;
       if (lane == 0) flag[hq] = rescaled;
-      __syncthreads();  // barrier B
-      // ---- phase 2 ----
-      mix(tiles + (it % NBUF) * BUF_BYTES);
-      if (it + 1 < ntiles) {
-        S = partial_scores<QK_O_STEPS, false>(tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q,
-                                              nullptr, lane);
-#pragma unroll
-        for (int j4 = 0; j4 < 4; j4++) {
-          const float4 o = sx_w[64 * j4];
-          S[4 * j4] += o.x;
-          S[4 * j4 + 1] += o.y;
-          S[4 * j4 + 2] += o.z;
-          S[4 * j4 + 3] += o.w;
+      // Between its multiplies this wave stages rows 4k+ow of tile it+2
+      // into the buffer tile it-1 used (free since barrier A): the time an
+      // instruction waits to enter the vector-memory pipeline then overlaps
+      // the MFMAs instead of stalling every wave after the barrier.
+      floatx16 Sn;
+      {
+        const char* buf = tiles + ((it + 1) % NBUF) * BUF_BYTES;
+        if (it + 2 < ntiles) {
+          const int ow = wave - 4;
+          const uint32_t dst = tiles_addr + ((it + 2) % NBUF) * BUF_BYTES;
+          const int srow0 = row_begin + (it + 2) * TILE;
+          constexpr int NSTAGE = TILE / 4 + 1;
+          static_assert(QK_O_STEPS >= NSTAGE, "owner k-steps must cover its DMA");
+          Sn = partial_scores<QK_O_STEPS, false, O_RING, true>(buf, s_off, q, nullptr, lane,
+                                                               [&](int j) {
+            if (j < NSTAGE)
+              stage_step<SPARSE, 4>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0, row_end,
+                                    row_begin, dst, ow, lane);
+          });
+        } else {
+          Sn = partial_scores<QK_O_STEPS, false, O_RING, true>(buf, s_off, q, nullptr, lane,
+                                                               [](int) {});
         }
+      }
+      __syncthreads();  // barrier B
+      // ---- phase 2: mix of tile it; scores of tile it+1 completed ----
+      mix(tiles + (it % NBUF) * BUF_BYTES);
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const float4 o = sx_w[64 * j4];
+        S[4 * j4] = Sn[4 * j4] + o.x;
+        S[4 * j4 + 1] = Sn[4 * j4 + 1] + o.y;
+        S[4 * j4 + 2] = Sn[4 * j4 + 2] + o.z;
+        S[4 * j4 + 3] = Sn[4 * j4 + 3] + o.w;
       }
     }
   }
@@ -518,7 +574,7 @@ __device__ __forceinline__ void st_elem(uint16_t* p, int64_t i, float v) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) void merge_splits_kernel(const T* __restrict__ ws_o,
+__global__ __launch_bounds__(64) void merge_splits_f32_kernel(const T* __restrict__ ws_o,
                                                           const float* __restrict__ ws_lse,
                                                           int S, int64_t BH, T* __restrict__ out,
                                                           float* __restrict__ lse) {
@@ -539,6 +595,51 @@ __global__ __launch_bounds__(64) void merge_splits_kernel(const T* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; i++) st_elem(out, bh * D_C + c0 + i, acc[i] * inv);
   if (threadIdx.x == 0 && lse) lse[bh] = mx + logf(wsum);
+}
+
+// bf16 partials: 64 lanes per (b, h) row, 8 latent features (16 bytes) per
+// lane, four rows per workgroup. Splits are taken MERGE_CHUNK at a time with
+// every load of a chunk issued before its first use (indices past the last
+// split are clamped and weighted zero).
+constexpr int MERGE_CHUNK = 8;
+__global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* __restrict__ ws_o,
+                                                                const float* __restrict__ ws_lse,
+                                                                int S, int64_t BH,
+                                                                uint16_t* __restrict__ out,
+                                                                float* __restrict__ lse) {
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;
+  const int c0 = (threadIdx.x & 63) * 8;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; s++) mx = fmaxf(mx, ws_lse[s * BH + bh]);
+  float wsum = 0.f;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
+    u32x4 v[MERGE_CHUNK];
+    float lv[MERGE_CHUNK];
+#pragma unroll
+    for (int j = 0; j < MERGE_CHUNK; j++) {
+      const int64_t sj = min(s0 + j, S - 1);
+      v[j] = ld16(ws_o + (sj * BH + bh) * D_C + c0);
+      lv[j] = ws_lse[sj * BH + bh];
+    }
+#pragma unroll
+    for (int j = 0; j < MERGE_CHUNK; j++) {
+      const float w = s0 + j < S ? __expf(lv[j] - mx) : 0.f;
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        acc[2 * i] = fmaf(w, __uint_as_float(v[j][i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(v[j][i] & 0xFFFF0000u), acc[2 * i + 1]);
+      }
+    }
+  }
+  const float inv = 1.f / wsum;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  st16(out + bh * D_C + c0, o);
+  if ((threadIdx.x & 63) == 0 && lse) lse[bh] = mx + logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,11 +733,11 @@ hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream
   if (e != hipSuccess || p.num_splits == 1) return e;
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
   if (is_bf16)
-    hipLaunchKernelGGL(merge_splits_kernel<uint16_t>, dim3(static_cast<unsigned>(BH)), dim3(64), 0,
-                       stream, static_cast<const uint16_t*>(p.ws_o), p.ws_lse, p.num_splits, BH,
-                       static_cast<uint16_t*>(p.out_lat), p.lse);
+    hipLaunchKernelGGL(merge_splits_bf16_kernel, dim3(static_cast<unsigned>((BH + 3) / 4)),
+                       dim3(256), 0, stream, static_cast<const uint16_t*>(p.ws_o), p.ws_lse,
+                       p.num_splits, BH, static_cast<uint16_t*>(p.out_lat), p.lse);
   else
-    hipLaunchKernelGGL(merge_splits_kernel<float>, dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+    hipLaunchKernelGGL(merge_splits_f32_kernel<float>, dim3(static_cast<unsigned>(BH)), dim3(64), 0,
                        stream, static_cast<const float*>(p.ws_o), p.ws_lse, p.num_splits, BH,
                        static_cast<float*>(p.out_lat), p.lse);
   return hipGetLastError();
