@@ -37,8 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
-                    help="decode workload (2: B=32 T=4096; 3: B=4 T=32768; 4: sparse fp8)")
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="2: decode B=32 T=4096 (default); 3: decode B=4 T=32768; "
+                         "4: sparse top-2048 decode with fp8 weights; 5: KV reconstruction N=8192")
     ap.add_argument("--min-replica-bytes", type=float, default=1.1e9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -110,10 +111,69 @@ def cpu_baseline(cfg, inp):
                       f"fp64 C oracle, OpenMP over (sequence, head)"}
 
 
+def reconstruct_main(args, torch, mla, synth):
+    """Config 5: the naive path's KV reconstruction, one call per step."""
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[5]
+    N, n_h = cfg["N"], cfg["n_h"]
+    inp = synth.config_inputs(5)
+    base = {k: v.to(dev) for k, v in inp.items()}
+    per_rep = sum(v.numel() * v.element_size() for v in base.values())
+    R = max(2, int(-(-args.min_replica_bytes // per_rep)))
+    reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    K = torch.empty((N, n_h, 192), dtype=torch.bfloat16, device=dev)
+    V = torch.empty((N, n_h, 128), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        x = reps[i % R]
+        mla.mla_kv_reconstruct(x["c"], x["k_rope"], x["wkv_b"], K, V)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    nbytes = (N * 512 + N * 64 + n_h * 256 * 512 + N * n_h * (192 + 128)) * 2
+    flops = 2 * N * 512 * n_h * 256
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "MLA KV reconstruction: token·heads/s and % of MFMA roofline",
+        "value": N * n_h / (ms * 1e-3), "unit": "token·heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; no datasets or trained weights)",
+        "config": {"workload": cfg["name"], "N": N, "n_h": n_h, "input_replicas": R},
+        "roofline": {"bound": "mfma", "kernel": "mla_kv_reconstruct", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": ms * 1e3,
+                     "roofline_us": roofline_time_s(nbytes, flops) * 1e6},
+        "published_baseline": "none: the source pages print no throughput figures",
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        n = 64  # rows of the sample: about 10-30 s of fp64 work on the host
+        t = time.perf_counter()
+        oracle.kv_reconstruct(inp["c"][:n], inp["k_rope"][:n], inp["wkv_b"], n_h)
+        dt = time.perf_counter() - t
+        line["cpu_baseline"] = {"value": n * n_h / dt, "unit": "token·heads/s", "cores": cores,
+                                "kind": "oracle", "seconds": round(dt, 3),
+                                "sample": f"{n} of the {N} tokens, all {n_h} heads, fp64 C oracle"}
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not "
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
                           "supported (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -123,6 +183,8 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.config == 5:
+        return reconstruct_main(args, torch, mla, synth)
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]
     B, n_h, T = cfg["B"], cfg["n_h"], cfg["T"]

@@ -413,5 +413,5 @@ def test_page_counts():
     inp = synth.decode_inputs(2, 2, 33)
     cache = inp["cache"]
     assert cache.numel() * cache.element_size() == 2 * 33 * (512 + 64) * 2
-    # the BASELINE decode workload: 32 x 4096 x 576 x 2 bytes
+    # the B=32, T=4096 decode workload: 32 x 4096 x 576 x 2 bytes
     assert 32 * 4096 * (512 + 64) * 2 == 150_994_944
