@@ -45,10 +45,45 @@ __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Raw buffer resource (base, no stride, 2^31-1 bytes, 32-bit format) in SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));
+  r[2] = 0x7FFFFFFF;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane i's 16 bytes at (rsrc base + soff + voff) land at LDS byte
+// lds_dst + 16*i. Issued from inline assembly so the compiler does not
+// serialise consecutive LDS-DMA loads; it has no register outputs, and the
+// caller waits with an explicit s_waitcnt vmcnt before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// 16-byte read of a __shared__ object through a generic pointer into it.
+__device__ __forceinline__ u32x4 ld_lds16(const char* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
 
 }  // namespace mla

@@ -68,7 +68,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // LDS tile layout.
 // Latent: row r occupies a 68-chunk (1088-byte) slot and its 64 data chunks
@@ -97,34 +96,6 @@ __device__ __forceinline__ int pi_row(int i) {
 __device__ __forceinline__ int tau_blk(int beta) { return 4 * (beta & 1) + (beta >> 1); }
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-
-// Raw buffer resource (base, no stride, 2^31-1 bytes, 32-bit format) in SGPRs.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));
-  r[2] = 0x7FFFFFFF;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
-// lane i's 16 bytes at (rsrc base + soff + voff) land at LDS byte
-// lds_dst + 16*i. Issued from inline assembly so the compiler does not
-// serialise consecutive LDS-DMA loads; it has no register outputs, and the
-// caller waits with an explicit s_waitcnt vmcnt before the barrier that
-// publishes the data.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
-}
 
 __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lo));

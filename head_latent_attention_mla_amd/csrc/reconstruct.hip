@@ -7,147 +7,237 @@
 //   kv[n,h,e] = sum_c wkv_b[h*256 + e, c] * c[n,c]
 //   K[n,h,:] = [kv[n,h,0:128] ; k_rope[n,:]],   V[n,h,:] = kv[n,h,128:256]
 //
-// A [N x 512] x [512 x n_h*256] GEMM (K = 512 is short) whose epilogue routes
-// each 128-feature half of a head to K or V, plus a 64-feature copy of k_rope
-// into every head's key. bf16 path: workgroup tile = 128 features (one half
-// of one head) x 256 tokens, 4 waves of 64 x 128, v_mfma_f32_32x32x16_bf16
-// with M = features, N = tokens, K = latent. Both operands are K-contiguous
-// in memory; 32-wide K slices are staged HBM -> LDS with
-// global_load_lds_dwordx4 (double-buffered, XOR-swizzled against bank
-// conflicts). The A-row permutation pi gives each lane 16 consecutive output
-// features of one token, i.e. two 16-byte stores.
+// A [N x 512] x [512 x n_h*256] GEMM (K = 512 is short) that writes 671 MB at
+// N = 8192, n_h = 128: its floor is the MFMA work and the output writes
+// together, so the kernel keeps both busy at once.
+//
+// bf16 path: a persistent kernel, one workgroup of 4 waves per CU, looping
+// over tiles of one head (256 features: the 128 k_nope rows then the 128 v
+// rows) x 256 tokens. Wave (wm, wn) accumulates features 128wm.. x tokens
+// 128wn.. (4 x 4 v_mfma_f32_32x32x16_bf16 tiles, 256 accumulator registers;
+// M = features, N = tokens, K = latent). The latent axis is staged in
+// 32-wide slices (32 KB: 256 weight rows + 256 token rows, 64 bytes each)
+// into four LDS buffers by LDS-DMA issued from inline assembly, three slices
+// ahead of the multiplies and across tile boundaries, so ~96 KB per CU stay
+// in flight. The tile's rotary rows ride along with slices 4..11 into a
+// fifth 32 KB buffer. A tile's epilogue issues its stores (K, V and the
+// rotary copy) and moves straight on: they drain while the next tile
+// multiplies. Every wave issues the same number of memory instructions in
+// the same order (tail tokens re-read and re-write the last token's row with
+// identical values), which makes the vmcnt bookkeeping exact.
+// The A-row permutation pi gives each lane 16 consecutive output features
+// of one token, i.e. two 16-byte stores.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 
 namespace {
-constexpr int RT_TOK = 256;                  // tokens per workgroup
-constexpr int RT_FEAT = 128;                 // features per workgroup
-constexpr int RT_KC = 32;                    // latent features per stage
-constexpr int A_CHUNKS = RT_FEAT * RT_KC / 8;  // 512 16-byte chunks
-constexpr int B_CHUNKS = RT_TOK * RT_KC / 8;   // 1024
-constexpr int STAGE_BYTES = (A_CHUNKS + B_CHUNKS) * 16;  // 24 KiB
+constexpr int RC_TOK = 256;                 // tokens per tile
+constexpr int RC_FEAT = ROWS_PER_HEAD;      // 256 features per tile (one head)
+constexpr int RC_KC = 32;                   // latent features per stage
+constexpr int RC_NSTAGE = D_C / RC_KC;      // 16 stages per tile
+constexpr int RC_NBUF = 4;                  // stage buffers
+constexpr int RC_AHEAD = RC_NBUF - 1;       // stages in flight ahead of the multiplies
+constexpr int RC_STAGE_BYTES = (RC_FEAT + RC_TOK) * RC_KC * 2;  // 32 KiB
+constexpr int RC_ROPE_BYTES = RC_TOK * D_R * 2;                 // 32 KiB
+constexpr int RC_LOADS = RC_STAGE_BYTES / 1024 / 4;             // 8 DMA per wave per stage
+constexpr int RC_ROPE_FIRST = 4;            // stages 4..11 also carry one rotary DMA
+constexpr int RC_STORES = 4 * 4 * 2 + RC_TOK * D_R * 2 / 16 / 256;  // 40 per wave per tile
 
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int pi_row(int i) {
   return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 }
+// DMA instructions per wave of the group that stages slice s of a tile
+constexpr int rc_loads(int s) {
+  return RC_LOADS + (s >= RC_ROPE_FIRST && s < RC_ROPE_FIRST + 8 ? 1 : 0);
+}
+// s_waitcnt vmcnt(N) at the top of stage s: the group of stage s must have
+// landed; the newer memory instructions allowed in flight are the groups of
+// stages s+1 and s+2 and, in the first three stages of a tile, the previous
+// tile's epilogue stores (issued after group s+2 of tile i-1 = group 2 of
+// tile i, before group 3). `prev` is false on a workgroup's first tile (no
+// previous stores), `last` true on its last tile (no groups past stage 15).
+constexpr int rc_wait(int s, bool prev, bool last) {
+  auto L = [&](int t) { return (last && t >= RC_NSTAGE) ? 0 : rc_loads(t % RC_NSTAGE); };
+  const int S = prev ? RC_STORES : 0;
+  if (s == 0) return L(1) + L(2) + S;
+  if (s == 1) return L(2) + S + L(3);
+  if (s == 2) return S + L(3) + L(4);
+  return L(s + 1) + L(s + 2);
+}
 }  // namespace
 
-__device__ __forceinline__ void rc_issue_stage(const uint16_t* wsrc, const uint16_t* xsrc,
-                                               int64_t N, int64_t tok0, int k0, char* stage,
-                                               int wave, int lane) {
-  // A: 128 feature rows x 4 chunks; B: 256 token rows x 4 chunks
-#pragma unroll
-  for (int k = 0; k < A_CHUNKS / 256; k++) {
-    const int blk = k * 4 + wave;
-    const int pch = blk * 64 + lane;
-    const int row = pch >> 2;
-    const int c = (pch & 3) ^ swz4(row);
-    __builtin_amdgcn_global_load_lds(wsrc + static_cast<int64_t>(row) * D_C + k0 + c * 8,
-                                     (lds_void*)(stage + blk * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < B_CHUNKS / 256; k++) {
-    const int blk = k * 4 + wave;
-    const int pch = blk * 64 + lane;
-    const int row = pch >> 2;
-    const int c = (pch & 3) ^ swz4(row);
-    int64_t tk = tok0 + row;
-    tk = tk < N ? tk : N - 1;  // tail tokens load a valid row; results are not stored
-    __builtin_amdgcn_global_load_lds(xsrc + tk * D_C + k0 + c * 8,
-                                     (lds_void*)(stage + A_CHUNKS * 16 + blk * 1024),
-                                     16, 0, 0);
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void kv_reconstruct_bf16_kernel(
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate out of range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Stage slice k0..k0+31 of the head's 256 weight rows (w_d) and the tile's
+// 256 token rows (x_d; rows past last_row re-read it) into `stage`: chunk j
+// (16 bytes) of row r lands at LDS chunk 4r + (j ^ swz4(r)), weight rows
+// first. Eight DMA instructions per wave.
+__device__ __forceinline__ void rc_stage(i32x4 w_d, i32x4 x_d, int last_row, int k0,
+                                         uint32_t stage, int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int blk = k * 4 + wave;  // 1 KB block of the stage
+    const int pch = (blk & 15) * 64 + lane;
+    const int row = pch >> 2;
+    const int c = (pch & 3) ^ swz4(row);
+    if (k < 4) {
+      dma16(w_d, stage + blk * 1024, static_cast<uint32_t>(row * (D_C * 2) + k0 * 2 + c * 16), 0);
+    } else {
+      const int r = row < last_row ? row : last_row;
+      dma16(x_d, stage + blk * 1024, static_cast<uint32_t>(r * (D_C * 2) + k0 * 2 + c * 16), 0);
+    }
+  }
+}
+
+// Rotary rows of the tile (contiguous 256 x 128 bytes; rows past last_row
+// re-read it): 1 KB block q = 4j + wave, one DMA instruction.
+__device__ __forceinline__ void rc_rope(i32x4 r_d, int last_row, int j, uint32_t rope,
+                                        int wave, int lane) {
+  const int q = 4 * j + wave;
+  const int tok = q * 8 + (lane >> 3);
+  const int t = tok < last_row ? tok : last_row;
+  dma16(r_d, rope + q * 1024, static_cast<uint32_t>(t * (D_R * 2) + (lane & 7) * 16), 0);
+}
+
+__global__ __launch_bounds__(256, 1) void kv_reconstruct_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ k_rope,
     const uint16_t* __restrict__ w, uint16_t* __restrict__ Kout, uint16_t* __restrict__ Vout,
     int64_t N, int n_h) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];
-  const int ntt = static_cast<int>((N + RT_TOK - 1) / RT_TOK);
-  const int tt = blockIdx.x % ntt;
-  const int hh = blockIdx.x / ntt;  // head * 2 + half
-  const int h = hh >> 1, half = hh & 1;
-  const int64_t tok0 = static_cast<int64_t>(tt) * RT_TOK;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) char lds[RC_NBUF * RC_STAGE_BYTES + RC_ROPE_BYTES];
+  const int ntt = static_cast<int>((N + RC_TOK - 1) / RC_TOK);
+  const int ntiles = ntt * n_h;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int wf = wave & 1, wn = wave >> 1;
-  const uint16_t* wsrc = w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + half * 128) * D_C;
+  const int wm = wave & 1, wn = wave >> 1;  // feature half (k_nope / v), token half
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const uint32_t rope_lds = lds0 + RC_NBUF * RC_STAGE_BYTES;
+  const char* rope_buf = lds + RC_NBUF * RC_STAGE_BYTES;
+  // this workgroup's tiles: t = blockIdx.x + i * gridDim.x, i < my_tiles;
+  // tile t = (head t / ntt, token tile t % ntt)
+  const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                       static_cast<int>(gridDim.x);
+  if (my_tiles <= 0) return;
 
-  floatx16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = floatx16{};
+  struct Tile {
+    i32x4 w_d, x_d, r_d;
+    int last_row, h;
+    int64_t tok0;
+  };
+  auto tile_of = [&](int i) {
+    Tile T;
+    const int t = static_cast<int>(blockIdx.x) + i * static_cast<int>(gridDim.x);
+    T.h = t / ntt;
+    T.tok0 = static_cast<int64_t>(t % ntt) * RC_TOK;
+    T.w_d = make_rsrc(w + static_cast<int64_t>(T.h) * ROWS_PER_HEAD * D_C);
+    T.x_d = make_rsrc(x + T.tok0 * D_C);
+    T.r_d = make_rsrc(k_rope + T.tok0 * D_R);
+    T.last_row = static_cast<int>(N - 1 - T.tok0 < RC_TOK - 1 ? N - 1 - T.tok0 : RC_TOK - 1);
+    return T;
+  };
+  // the DMA group of stage s of tile T into buffer slot
+  auto issue = [&](const Tile& T, int s, int slot) {
+    rc_stage(T.w_d, T.x_d, T.last_row, s * RC_KC, lds0 + slot * RC_STAGE_BYTES, wave, lane);
+    if (s >= RC_ROPE_FIRST && s < RC_ROPE_FIRST + 8)
+      rc_rope(T.r_d, T.last_row, s - RC_ROPE_FIRST, rope_lds, wave, lane);
+  };
 
-  rc_issue_stage(wsrc, x, N, tok0, 0, lds, wave, lane);
-  constexpr int NSTAGE = D_C / RT_KC;  // 16
-  for (int st = 0; st < NSTAGE; st++) {
-    char* cur = lds + (st & 1) * STAGE_BYTES;
-    if (st + 1 < NSTAGE) {
-      rc_issue_stage(wsrc, x, N, tok0, (st + 1) * RT_KC, lds + ((st + 1) & 1) * STAGE_BYTES, wave,
-                     lane);
-      __builtin_amdgcn_s_waitcnt(0xF70 | ((A_CHUNKS + B_CHUNKS) / 256));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0xF70);
-    }
-    __syncthreads();
+  floatx16 acc[4][4];
+  Tile cur = tile_of(0);
+  // prologue: groups of stages 0..2 of the first tile (slots 0..2)
 #pragma unroll
-    for (int ks = 0; ks < RT_KC / 16; ks++) {
-      const int c = 2 * ks + g;
-      bf16x8 a[2], bb[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const int row = wf * 64 + mt * 32 + pi_row(n);
-        a[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(cur + (row * 4 + (c ^ swz4(row))) * 16));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; nt++) {
-        const int row = wn * 128 + nt * 32 + n;
-        bb[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(cur + A_CHUNKS * 16 +
-                                                           (row * 4 + (c ^ swz4(row))) * 16));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma32x32x16(a[mt], bb[nt], acc[mt][nt]);
-    }
-    __syncthreads();
-  }
+  for (int s = 0; s < RC_AHEAD; s++) issue(cur, s, s);
 
-  // epilogue: lane (token n of N-tile nt, half g) holds features 16g..16g+15
-  // of M-tile mt
+  int gstage = 0;  // stages begun so far (the buffer slot is gstage % RC_NBUF)
+  for (int i = 0; i < my_tiles; i++) {
+    const bool prev = i > 0, last = i + 1 == my_tiles;
+    Tile nxt = last ? cur : tile_of(i + 1);
 #pragma unroll
-  for (int nt = 0; nt < 4; nt++) {
-    const int64_t tk = tok0 + wn * 128 + nt * 32 + n;
-    if (tk >= N) continue;
+    for (int a = 0; a < 4; a++)
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      const int e = wf * 64 + mt * 32 + 16 * g;  // feature within the half
-      u32x4 v0, v1;
+      for (int b = 0; b < 4; b++) acc[a][b] = floatx16{};
+    static_for<0, RC_NSTAGE>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      // group s landed; stage s-1's buffer is free for the group 3 ahead
+      if (prev && !last) wait_vm<rc_wait(s, true, false)>();
+      else if (prev) wait_vm<rc_wait(s, true, true)>();
+      else if (!last) wait_vm<rc_wait(s, false, false)>();
+      else wait_vm<rc_wait(s, false, true)>();
+      __syncthreads();
+      const int ahead = s + RC_AHEAD;
+      const int slot_ahead = (gstage + RC_AHEAD) & (RC_NBUF - 1);
+      if (ahead < RC_NSTAGE)
+        issue(cur, ahead, slot_ahead);
+      else if (!last)
+        issue(nxt, ahead - RC_NSTAGE, slot_ahead);
+      const char* buf = lds + (gstage & (RC_NBUF - 1)) * RC_STAGE_BYTES;
+      gstage++;
 #pragma unroll
-      for (int w2 = 0; w2 < 4; w2++) {
-        v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2], acc[mt][nt][2 * w2 + 1]);
-        v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2], acc[mt][nt][8 + 2 * w2 + 1]);
+      for (int ks = 0; ks < RC_KC / 16; ks++) {
+        const int c = 2 * ks + g;
+        bf16x8 av[4], bv[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const int row = wm * 128 + mt * 32 + pi_row(n);
+          av[mt] = as_bf16x8(ld_lds16(buf + (row * 4 + (c ^ swz4(row))) * 16));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++) {
+          const int row = wn * 128 + nt * 32 + n;
+          bv[nt] = as_bf16x8(ld_lds16(buf + RC_FEAT * RC_KC * 2 + (row * 4 + (c ^ swz4(row))) * 16));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma32x32x16(av[mt], bv[nt], acc[mt][nt]);
       }
-      uint16_t* dst = half == 0 ? Kout + (tk * n_h + h) * (D_N + D_R) + e
-                                : Vout + (tk * n_h + h) * D_V + e;
-      st16(dst, v0);
-      st16(dst + 8, v1);
-    }
-  }
-  if (half == 0) {
-    // K[n,h,128:192] = k_rope[n,:]: 8 chunks of 16 bytes per token
+    });
+    // epilogue: lane (token n of N-tile nt, half g) holds features
+    // 32mt + 16g .. +15 of half wm; tail tokens rewrite the last token
 #pragma unroll
-    for (int k = 0; k < RT_TOK * 8 / 256; k++) {
-      const int idx = k * 256 + threadIdx.x;
-      const int64_t tk = tok0 + (idx >> 3);
-      const int c = idx & 7;
-      if (tk < N) st16(Kout + (tk * n_h + h) * (D_N + D_R) + D_N + c * 8, ld16(k_rope + tk * D_R + c * 8));
+    for (int nt = 0; nt < 4; nt++) {
+      const int64_t tk = cur.tok0 + (min(wn * 128 + nt * 32 + n, cur.last_row));
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const int e = mt * 32 + 16 * g;
+        u32x4 v0, v1;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; w2++) {
+          v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2], acc[mt][nt][2 * w2 + 1]);
+          v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2], acc[mt][nt][8 + 2 * w2 + 1]);
+        }
+        uint16_t* dst = wm == 0 ? Kout + (tk * n_h + cur.h) * (D_N + D_R) + e
+                                : Vout + (tk * n_h + cur.h) * D_V + e;
+        st16(dst, v0);
+        st16(dst + 8, v1);
+      }
     }
+    // K[n,h,128:192] = k_rope[n,:] from the staged rows: 8 chunks per token
+#pragma unroll
+    for (int k = 0; k < RC_TOK * 8 / 256; k++) {
+      const int idx = k * 256 + static_cast<int>(threadIdx.x);
+      const int tl = min(idx >> 3, cur.last_row);
+      const u32x4 v = ld_lds16(rope_buf + (idx >> 3) * 128 + (idx & 7) * 16);
+      st16(Kout + ((cur.tok0 + tl) * n_h + cur.h) * (D_N + D_R) + D_N + (idx & 7) * 8, v);
+    }
+    cur = nxt;
   }
 }
 
@@ -174,12 +264,27 @@ __global__ __launch_bounds__(256) void kv_reconstruct_f32_kernel(const float* __
   if (e < D_R) Kout[(tk * n_h + h) * (D_N + D_R) + D_N + e] = k_rope[tk * D_R + e];
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cache[64] = {0};
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  return cus;
+}
+
 hipError_t launch_kv_reconstruct(const void* c, const void* k_rope, const void* wkv_b, void* K,
                                  void* V, int64_t N, int n_h, bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int64_t ntt = (N + RT_TOK - 1) / RT_TOK;
-    hipLaunchKernelGGL(kv_reconstruct_bf16_kernel, dim3(static_cast<unsigned>(ntt * n_h * 2)),
-                       dim3(256), 0, stream, static_cast<const uint16_t*>(c),
+    const int64_t tiles = (N + RC_TOK - 1) / RC_TOK * n_h;
+    const int64_t grid = tiles < cu_count() ? tiles : cu_count();
+    hipLaunchKernelGGL(kv_reconstruct_bf16_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(c),
                        static_cast<const uint16_t*>(k_rope), static_cast<const uint16_t*>(wkv_b),
                        static_cast<uint16_t*>(K), static_cast<uint16_t*>(V), N, n_h);
   } else {
