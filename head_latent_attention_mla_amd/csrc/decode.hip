@@ -569,9 +569,10 @@ __global__ __launch_bounds__(64) void merge_splits_f32_kernel(const T* __restric
 }
 
 // bf16 partials: 64 lanes per (b, h) row, 8 latent features (16 bytes) per
-// lane, four rows per workgroup. Splits are taken MERGE_CHUNK at a time with
-// every load of a chunk issued before its first use (indices past the last
-// split are clamped and weighted zero).
+// lane, four rows per workgroup. Splits are taken MERGE_CHUNK at a time; a
+// chunk's log-sum-exps and partials are loaded together (one memory round
+// trip per chunk: indices past the last split are clamped and weighted
+// zero) and folded in with a running maximum.
 constexpr int MERGE_CHUNK = 8;
 __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_lse,
@@ -581,9 +582,7 @@ __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* 
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
   const int c0 = (threadIdx.x & 63) * 8;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; s++) mx = fmaxf(mx, ws_lse[s * BH + bh]);
-  float wsum = 0.f;
+  float mx = -INFINITY, wsum = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
     u32x4 v[MERGE_CHUNK];
@@ -591,9 +590,17 @@ __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < MERGE_CHUNK; j++) {
       const int64_t sj = min(s0 + j, S - 1);
-      v[j] = ld16(ws_o + (sj * BH + bh) * D_C + c0);
       lv[j] = ws_lse[sj * BH + bh];
+      v[j] = ld16(ws_o + (sj * BH + bh) * D_C + c0);
     }
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < MERGE_CHUNK; j++) cm = fmaxf(cm, lv[j]);
+    const float f = __expf(mx - cm);  // 0 on the first chunk (mx = -inf)
+    wsum *= f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] *= f;
+    mx = cm;
 #pragma unroll
     for (int j = 0; j < MERGE_CHUNK; j++) {
       const float w = s0 + j < S ? __expf(lv[j] - mx) : 0.f;

@@ -26,9 +26,15 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
   const int nbt = (B + 31) >> 5;
-  const int bt = blockIdx.x % nbt;
-  const int dt = (blockIdx.x / nbt) & 3;
-  const int h = blockIdx.x / (nbt * 4);
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order; when the
+  // heads split evenly, XCD x takes every workgroup of heads h = x (mod 8),
+  // so the four quarters of each weight row are fetched by one XCD.
+  int L = blockIdx.x;
+  if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (static_cast<int>(gridDim.x) >> 3);
+  const int bt = L % nbt;
+  const int dt = (L / nbt) & 3;
+  const int hh = L / (nbt * 4);  // head index in XCD-grouped order
+  const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
   // rows past B load row B-1 (unconditional loads keep all 16 in flight);
   // their results are never stored
   const int b = min(bt * 32 + n, B - 1);
