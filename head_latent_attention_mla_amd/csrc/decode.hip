@@ -53,7 +53,7 @@ constexpr int ROPE_BYTES = TILE * D_R * 2;        // 4 KiB rotary region
 constexpr int BUF_BYTES = LAT_BYTES + ROPE_BYTES; // one staged tile
 constexpr int NBUF = 3;                           // tiles in LDS (2 in flight)
 constexpr int MAX_SPARSE_ROWS = 1024;             // staged top-k indices per split
-constexpr int QK_P_STEPS = 19;                    // latent k-steps of the partner wave
+constexpr int QK_P_STEPS = 21;                    // latent k-steps of the partner wave
 constexpr int QK_O_STEPS = D_C / 16 - QK_P_STEPS; // latent k-steps of the owner wave
 constexpr int QK_ROPE_STEPS = D_R / 16;           // 4 rotary k-steps (partner wave)
 #ifndef MLA_P_RING
@@ -387,8 +387,23 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     for (int it = 0; it < ntiles; it++) {
       top_of_tile();
       if (it + 1 < ntiles) {
-        const floatx16 Sp = partial_scores<QK_P_STEPS, true, P_RING, true>(
-            tiles + ((it + 1) % NBUF) * BUF_BYTES, s_off, q, qpe_w, lane, [](int) {});
+        const char* buf = tiles + ((it + 1) % NBUF) * BUF_BYTES;
+        floatx16 Sp;
+        if (it + 2 < ntiles) {
+          // this wave's share of the DMA of tile it+2 (latent rows 8k+wave)
+          // between its multiplies; the owners stage the rest
+          const uint32_t dst = tiles_addr + ((it + 2) % NBUF) * BUF_BYTES;
+          const int srow0 = row_begin + (it + 2) * TILE;
+          Sp = partial_scores<QK_P_STEPS, true, P_RING, true>(buf, s_off, q, qpe_w, lane,
+                                                              [&](int j) {
+            if (j < TILE / NWAVES)
+              stage_step<SPARSE, NWAVES>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0,
+                                         row_end, row_begin, dst, wave, lane);
+          });
+        } else {
+          Sp = partial_scores<QK_P_STEPS, true, P_RING, true>(buf, s_off, q, qpe_w, lane,
+                                                              [](int) {});
+        }
 #pragma unroll
         for (int j4 = 0; j4 < 4; j4++)
           sx_w[64 * j4] = make_float4(Sp[4 * j4], Sp[4 * j4 + 1], Sp[4 * j4 + 2], Sp[4 * j4 + 3]);
@@ -451,24 +466,26 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       }
       if (g == 0) fac[hq * 32 + n] = f;
       if (lane == 0) flag[hq] = rescaled;
-      // Between its multiplies this wave stages rows 4k+ow of tile it+2
-      // into the buffer tile it-1 used (free since barrier A): the time an
-      // instruction waits to enter the vector-memory pipeline then overlaps
-      // the MFMAs instead of stalling every wave after the barrier.
+      // Between its multiplies this wave stages its share of tile it+2
+      // (latent rows 8k+wave and the rotary rows) into the buffer tile it-1
+      // used (free since barrier A): the time an instruction waits to enter
+      // the vector-memory pipeline then overlaps MFMAs instead of stalling
+      // every wave after the barrier. The partner waves stage the other
+      // latent rows.
       floatx16 Sn;
       {
         const char* buf = tiles + ((it + 1) % NBUF) * BUF_BYTES;
         if (it + 2 < ntiles) {
-          const int ow = wave - 4;
           const uint32_t dst = tiles_addr + ((it + 2) % NBUF) * BUF_BYTES;
           const int srow0 = row_begin + (it + 2) * TILE;
-          constexpr int NSTAGE = TILE / 4 + 1;
-          static_assert(QK_O_STEPS >= NSTAGE, "owner k-steps must cover its DMA");
           Sn = partial_scores<QK_O_STEPS, false, O_RING, true>(buf, s_off, q, nullptr, lane,
                                                                [&](int j) {
-            if (j < NSTAGE)
-              stage_step<SPARSE, 4>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0, row_end,
-                                    row_begin, dst, ow, lane);
+            if (j < TILE / NWAVES)
+              stage_step<SPARSE, NWAVES>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0,
+                                         row_end, row_begin, dst, wave, lane);
+            else if (j == TILE / NWAVES)  // the rotary rows 8(wave-4)..+7
+              stage_step<SPARSE, NWAVES>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0,
+                                         row_end, row_begin, dst, wave - 4, lane);
           });
         } else {
           Sn = partial_scores<QK_O_STEPS, false, O_RING, true>(buf, s_off, q, nullptr, lane,
