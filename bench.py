@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three times "
+                         "(the reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -70,8 +73,9 @@ def roofline_time_s(nbytes, flops):
 
 
 def traffic_record(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source (else None)."""
+    """HBM bytes per launch from committed rocprofv3 counter runs
+    (profiles/traffic.json), if they were taken on the current kernel
+    sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -79,9 +83,11 @@ def traffic_record(kernel_key):
         rec = json.load(f).get(kernel_key)
     if not rec:
         return None
-    src = os.path.join(ROOT, "head_latent_attention_mla_amd", "csrc", rec["source"])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return rec["bytes_per_launch"] if digest == rec["source_sha256_16"] else None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, "head_latent_attention_mla_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["sources_sha256_16"] else None
 
 
 def cpu_baseline(cfg, inp):
@@ -183,6 +189,14 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        return
     if args.config == 5:
         return reconstruct_main(args, torch, mla, synth)
     dev = torch.device("cuda:0")
@@ -237,7 +251,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # eager pass: events around each call (per-call durations, dominant kernel)
+    # eager pass: events around each call
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -248,26 +262,76 @@ def main():
     outup_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     eager_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
 
-    # timed region: whole steps replayed from HIP graphs (one per replica),
-    # bracketed by synchronisation
-    graphs = []
+    # per-call durations without host launch overhead: one HIP graph per call
+    # kind holding that call once per replica, replayed; events on the stream
+    # the graph (and so the kernels) run on
+    def call_absorb(r):
+        x = reps[r]
+        mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
+
+    def call_decode(r):
+        x = reps[r]
+        mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
+                                   x["cache"][..., 512:], topk_idx=x["topk"], out_lat=o_lat,
+                                   workspace=ws)
+
+    def call_out_up(r):
+        x = reps[r]
+        mla.mla_out_up(o_lat, x["w"], out)
+
+    def graph_of(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i % R)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(g, rounds):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(rounds):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def graph_call_ms(fn):
+        # graphs of R and 3R calls: the difference cancels the fixed cost of
+        # launching a graph, leaving back-to-back kernel execution per call
+        g1, g3 = graph_of(fn, R), graph_of(fn, 3 * R)
+        rounds = max(2, args.steps // (2 * R))
+        return (replay_ms(g3, rounds) - replay_ms(g1, rounds)) / (rounds * 2 * R)
+
     if not args.no_graph:
-        for r in range(R):
-            gph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gph):
-                step(r)
-            graphs.append(gph)
-        for i in range(args.warmup):
-            graphs[i % R].replay()
+        absorb_ms = graph_call_ms(call_absorb)
+        decode_ms = graph_call_ms(call_decode)
+        outup_ms = graph_call_ms(call_out_up)
+
+    # timed region: exactly K whole steps, bracketed by synchronisation,
+    # replayed from HIP graphs that each hold R consecutive steps (one per
+    # input replica, as a multi-layer decode graph would) plus one graph for
+    # the remaining K mod R steps
+    full, rest = divmod(args.steps, R)
+    if not args.no_graph:
+        g_full = graph_of(step, R)
+        g_rest = graph_of(step, rest) if rest else None
+        for _ in range(max(1, args.warmup // R)):
+            g_full.replay()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % R].replay()
-        else:
+    if args.no_graph:
+        for i in range(args.steps):
             step(i)
+    else:
+        for _ in range(full):
+            g_full.replay()
+        if g_rest is not None:
+            g_rest.replay()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -305,7 +369,7 @@ def main():
                  "bytes": work["step_bytes"], "flops": work["step_flops"],
                  "GB_s": work["step_bytes"] / (ms_step * 1e-3) / 1e9,
                  "TFLOP_s": work["step_flops"] / (ms_step * 1e-3) / 1e12,
-                 "launch": "eager" if args.no_graph else "hip_graph_replay",
+                 "launch": "eager" if args.no_graph else f"hip_graph_replay ({R} steps per graph)",
                  "eager_step_us": eager_ms * 1e3,
                  "absorb_us": absorb_ms * 1e3, "decode_us": decode_ms * 1e3,
                  "out_up_us": outup_ms * 1e3},
