@@ -44,6 +44,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
+    ap.add_argument("--tp", type=int, default=1, metavar="G",
+                    help="one GPU's tensor-parallel share of a decode workload: 128/G heads "
+                         "(the whole cache is still read)")
+    ap.add_argument("--yarn", action="store_true",
+                    help="use the context-extended (YaRN) attention scale: "
+                         "max_seq_len 163840 > 4096, mscale 1, rope_factor 40")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times "
                          "(the reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -200,9 +206,17 @@ def main():
     if args.config == 5:
         return reconstruct_main(args, torch, mla, synth)
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[args.config]
+    cfg = dict(synth.CONFIGS[args.config])
+    if args.tp > 1:
+        if 128 % args.tp:
+            print(json.dumps({"error": "--tp must divide 128"}))
+            sys.exit(2)
+        cfg["n_h"] = 128 // args.tp
+        cfg["name"] += f", tensor-parallel share n_h=128/{args.tp}"
     B, n_h, T = cfg["B"], cfg["n_h"], cfg["T"]
-    inp = synth.config_inputs(args.config)
+    inp = synth.config_inputs(args.config, n_h=n_h)
+    scale = (mla.mla_softmax_scale(192, 163840, 4096, 1.0, 40.0) if args.yarn
+             else mla.mla_softmax_scale(192))
     sparse = "topk_idx" in inp
     rows = inp["topk_idx"].shape[1] if sparse else T
 
@@ -239,8 +253,8 @@ def main():
         if ev is not None:
             ev[1].record()
         mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
-                                   x["cache"][..., 512:], topk_idx=x["topk"], out_lat=o_lat,
-                                   workspace=ws)
+                                   x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
+                                   out_lat=o_lat, workspace=ws)
         if ev is not None:
             ev[2].record()
         mla.mla_out_up(o_lat, x["w"], out)
@@ -272,8 +286,8 @@ def main():
     def call_decode(r):
         x = reps[r]
         mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
-                                   x["cache"][..., 512:], topk_idx=x["topk"], out_lat=o_lat,
-                                   workspace=ws)
+                                   x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
+                                   out_lat=o_lat, workspace=ws)
 
     def call_out_up(r):
         x = reps[r]
@@ -342,7 +356,7 @@ def main():
     t_roof_step = roofline_time_s(work["step_bytes"], work["step_flops"])
     # dominant kernel: the latent attention call (split kernel + merge kernel)
     attn_gbs = work["attn_bytes"] / (decode_ms * 1e-3) / 1e9
-    traffic = traffic_record(f"decode_config{args.config}")
+    traffic = traffic_record(f"decode_config{args.config}" + (f"_tp{args.tp}" if args.tp > 1 else ""))
     line = {
         "metric": METRIC,
         "value": value,
@@ -356,7 +370,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; no datasets or trained weights)",
-        "config": {"workload": cfg["name"], "B": B, "n_h": n_h, "T": T,
+        "config": {"workload": cfg["name"], "B": B, "n_h": n_h, "T": T, "tp_share": args.tp,
+                   "attention_scale": scale,
                    "attended_positions": rows, "query_tokens": 1,
                    "fp8_weights": bool(cfg.get("fp8_weights", False)),
                    "decode_splits": splits, "input_replicas": R},

@@ -56,6 +56,8 @@ def library() -> ctypes.CDLL:
                                                P, P, P, Z, I, P]
         lib.mla_out_up.argtypes = [P, P, P, I, I, I, P]
         lib.mla_kv_reconstruct.argtypes = [P, P, P, P, P, L, I, I, P]
+        lib.mla_softmax_scale.argtypes = [I, L, L, F, F]
+        lib.mla_softmax_scale.restype = F
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
                      "mla_out_up", "mla_kv_reconstruct"):
             getattr(lib, name).restype = I
@@ -245,3 +247,11 @@ def mla_kv_reconstruct(c: torch.Tensor, k_rope: torch.Tensor, wkv_b: torch.Tenso
         _ptr(c), _ptr(k_rope), _ptr(wkv_b), _ptr(K), _ptr(V), N, n_h, _dtype_code(c),
         _stream(stream)))
     return K, V
+
+
+def mla_softmax_scale(qk_head_dim: int = 192, max_seq_len: int = 0, original_seq_len: int = 0,
+                      mscale: float = 1.0, rope_factor: float = 1.0) -> float:
+    """The attention scale (with the YaRN factor when max_seq_len exceeds
+    original_seq_len); see include/mla.h."""
+    return library().mla_softmax_scale(qk_head_dim, max_seq_len, original_seq_len, mscale,
+                                       rope_factor)

@@ -255,3 +255,15 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope, const void* wkv
 }
 
 }  // extern "C"
+
+extern "C" float mla_softmax_scale(int qk_head_dim, int64_t max_seq_len, int64_t original_seq_len,
+                                   float mscale, float rope_factor) {
+  if (qk_head_dim <= 0) return NAN;
+  double scale = 1.0 / std::sqrt(static_cast<double>(qk_head_dim));
+  if (max_seq_len > original_seq_len) {
+    if (!(rope_factor > 0.f)) return NAN;
+    const double ms = 0.1 * static_cast<double>(mscale) * std::log(static_cast<double>(rope_factor)) + 1.0;
+    scale *= ms * ms;
+  }
+  return static_cast<float>(scale);
+}

@@ -214,7 +214,9 @@ __device__ __forceinline__ floatx16 partial_scores(const char* buf, int s_off, c
   return sacc;
 }
 
-template <bool SPARSE>
+// FULL: every 128-head group holds 128 real heads (n_h % 128 == 0), which
+// removes the code for head quarters without heads.
+template <bool SPARSE, bool FULL>
 __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char tiles[NBUF * BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // partner partial scores
@@ -287,6 +289,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   float m = -INFINITY;  // owner waves: running max of scale*log2(e)*score
   float l = 0.f;        // owner waves: this lane's share of the running sum
   const float sl2 = p.scale * LOG2E;
+  // head quarters of this group that hold real heads (n_h need not fill
+  // 128): waves of the other quarters compute no scores and no softmax, and
+  // the mix skips their head tiles; they still stage their share of tiles
+  const int nact = FULL ? 4 : min(4, (p.n_h - hg * 128 + 31) >> 5);
+  const bool active = FULL || hq < nact;
 
   // ---- software-pipelined tile loop ---------------------------------------------
   // Entering iteration it: the owner waves hold the complete scores S of tile
@@ -306,6 +313,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   // tile 1 by all waves, then the barrier that publishes tile 0 (and the
   // staged rotary queries). In the loop only the owner waves stage tiles.
   auto tile0_wait = [&]() {
+    if (threadIdx.x < 4) flag[threadIdx.x] = 0;
     if (ntiles > 1)
       issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin + TILE, row_end,
                          row_begin, tiles_addr + BUF_BYTES, wave, lane);
@@ -330,7 +338,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
       for (int nt = 0; nt < 4; nt++) {
-        if (fl[nt]) {
+        if (nt < nact && fl[nt]) {
           const float fn = fac[nt * 32 + n];
           acc[0][nt] *= fn;
           acc[1][nt] *= fn;
@@ -346,6 +354,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
         A[mt][kk] = tr_pair(mp + 8704 * kk + 64 * mt, mp + 8704 * kk + 4368 + 64 * mt);
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
+      if (nt >= nact) break;
       const bf16x8 B0 = as_bf16x8(pb[(nt * 2 + 0) * 64 + lane]);
       const bf16x8 B1 = as_bf16x8(pb[(nt * 2 + 1) * 64 + lane]);
 #pragma unroll
@@ -357,7 +366,27 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   };
   float4* const sx_w = reinterpret_cast<float4*>(sx) + hq * 256 + lane;
 
-  if (kh == 0) {
+  if (!active) {
+    // ======== waves of a head quarter without heads: staging and mix only ========
+    tile0_wait();
+    __syncthreads();  // (partner scores of tile 0 published)
+    for (int it = 0; it < ntiles; it++) {
+      top_of_tile();
+      if (it + 2 < ntiles) {
+        const uint32_t dst = tiles_addr + ((it + 2) % NBUF) * BUF_BYTES;
+        const int srow0 = row_begin + (it + 2) * TILE;
+#pragma unroll
+        for (int j = 0; j < TILE / NWAVES; j++)
+          stage_step<SPARSE, NWAVES>(j, lat_d, rope_d, lat_rb, rope_rb, idx_lds, srow0, row_end,
+                                     row_begin, dst, wave, lane);
+        if (kh == 1)  // the owners stage the rotary rows 8(wave-4)..+7
+          stage_step<SPARSE, NWAVES>(TILE / NWAVES, lat_d, rope_d, lat_rb, rope_rb, idx_lds,
+                                     srow0, row_end, row_begin, dst, wave - 4, lane);
+      }
+      __syncthreads();  // barrier B
+      mix(tiles + (it % NBUF) * BUF_BYTES);
+    }
+  } else if (kh == 0) {
     // ======== partner waves: the first QK_P_STEPS latent k-steps and the rotary ones ==
     // query operands: k-step ks covers features 16ks..16ks+15, lane half g the
     // 8 at 16ks + 8g; rotary operands staged in LDS as [hq][k-step][lane]
@@ -508,7 +537,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
 
   // ---- epilogue -----------------------------------------------------------------
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
-  if (kh == 1) {
+  if (kh == 1 && active) {
     const float l_tot = pair_sum(l);
     if (g == 0) linv[hq * 32 + n] = 1.f / l_tot;
     if (g == 0 && head < p.n_h) {
@@ -717,10 +746,10 @@ hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream
   const int hgroups = (p.n_h + 127) / 128;
   if (is_bf16) {
     dim3 grid(p.num_splits, hgroups, p.B);
-    if (p.idx)
-      hipLaunchKernelGGL(decode_bf16_kernel<true>, grid, dim3(NWAVES * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL(decode_bf16_kernel<false>, grid, dim3(NWAVES * 64), 0, stream, p);
+    const bool full = p.n_h % 128 == 0;
+    auto kern = p.idx ? (full ? decode_bf16_kernel<true, true> : decode_bf16_kernel<true, false>)
+                      : (full ? decode_bf16_kernel<false, true> : decode_bf16_kernel<false, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(NWAVES * 64), 0, stream, p);
   } else {
     hipLaunchKernelGGL(decode_f32_kernel, dim3(p.num_splits, p.n_h, p.B), dim3(256), 0, stream, p);
   }

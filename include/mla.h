@@ -183,6 +183,19 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope,
                               const void* wkv_b, void* K, void* V, int64_t N,
                               int n_h, mla_dtype dt, hipStream_t stream);
 
+/*
+ * mla_softmax_scale — the attention scale to pass as `scale` to
+ * mla_decode_latent_attn ([KVL] mla-init excerpt): qk_head_dim^(-1/2)
+ * (192 here: 128 content + 64 rotary features), and, when the model runs
+ * past its original context (max_seq_len > original_seq_len), multiplied by
+ * mscale_eff^2 with mscale_eff = 0.1 * mscale * ln(rope_factor) + 1 (the YaRN
+ * extension). Pure host arithmetic in double, rounded to float; no GPU call.
+ * Returns NaN if qk_head_dim <= 0, or if the extension applies and
+ * rope_factor <= 0.
+ */
+float mla_softmax_scale(int qk_head_dim, int64_t max_seq_len, int64_t original_seq_len,
+                        float mscale, float rope_factor);
+
 #ifdef __cplusplus
 }
 #endif

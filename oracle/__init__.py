@@ -61,6 +61,8 @@ def _load():
         lib.orc_kv_reconstruct.argtypes = [P, P, I, P, I, L, I, I, I, I, I, P, P]
         lib.orc_decode_naive.argtypes = [P, P, I, P, P, I, L, L, L, L, P, I, I, I, I,
                                          I, I, I, I, P, I, D, P, P]
+        lib.orc_softmax_scale.argtypes = [I, L, L, D, D]
+        lib.orc_softmax_scale.restype = D
         for name in ("orc_dequant_fp8_block", "orc_absorb_q", "orc_latent_attention",
                      "orc_out_up", "orc_decode_absorbed", "orc_kv_reconstruct",
                      "orc_decode_naive"):
@@ -255,3 +257,11 @@ def kv_reconstruct(c, k_rope, w, n_h, d_n=D_N, d_v=D_V):
     _check(_load().orc_kv_reconstruct(_ptr(cc), _ptr(kr), _dt(cc), _ptr(W), _dt(W), N, n_h,
                                       d_c, d_r, d_n, d_v, _ptr(K), _ptr(V)), "kv_reconstruct")
     return K, V
+
+
+def softmax_scale(qk_head_dim=192, max_seq_len=0, original_seq_len=0, mscale=1.0,
+                  rope_factor=1.0) -> float:
+    """Attention scale of the mla-init excerpt (YaRN extension when
+    max_seq_len > original_seq_len), in double."""
+    return _load().orc_softmax_scale(qk_head_dim, max_seq_len, original_seq_len,
+                                     float(mscale), float(rope_factor))

@@ -405,3 +405,21 @@ int orc_decode_naive(const void* q_nope, const void* q_pe, int dt_q, const void*
   free(al);
   return rc;
 }
+
+/* ---- softmax scale ----------------------------------------------------------
+ * "DeepSeek-V3.2-Exp · Key–value latent", mla-init excerpt: the scale is
+ * qk_head_dim^(-1/2); when the model runs past its original context length
+ * it is multiplied by mscale^2 with mscale = 0.1 * m * ln(rope_factor) + 1.
+ * Returns NaN for a non-positive head dimension, or a non-positive
+ * rope_factor when the extension applies. */
+double orc_softmax_scale(int qk_head_dim, int64_t max_seq_len, int64_t original_seq_len,
+                         double m, double rope_factor) {
+  if (qk_head_dim <= 0) return NAN;
+  double scale = 1.0 / sqrt((double)qk_head_dim);
+  if (max_seq_len > original_seq_len) {
+    if (!(rope_factor > 0.0)) return NAN;
+    const double ms = 0.1 * m * log(rope_factor) + 1.0;
+    scale = scale * ms * ms;
+  }
+  return scale;
+}

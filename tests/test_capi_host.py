@@ -122,3 +122,16 @@ def test_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         binding.mla_absorb_q(torch.zeros(1, 16, 128, dtype=torch.bfloat16),
                              torch.zeros(16 * 256, 512, dtype=torch.bfloat16))
+
+
+def test_softmax_scale_matches_the_oracle():
+    import math
+    import oracle
+    cases = [(192, 0, 0, 1.0, 1.0), (192, 163840, 4096, 1.0, 40.0), (192, 4096, 4096, 1.0, 40.0),
+             (192, 163840, 4096, 0.707, 40.0), (128, 10, 5, 1.0, 4.0)]
+    for c in cases:
+        got = binding.mla_softmax_scale(*c)
+        ref = oracle.softmax_scale(*c)
+        assert abs(got - ref) <= 2.0 ** -24 * abs(ref), (c, got, ref)
+    assert math.isnan(binding.mla_softmax_scale(0))
+    assert math.isnan(binding.mla_softmax_scale(192, 2, 1, 1.0, -1.0))

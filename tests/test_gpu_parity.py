@@ -318,3 +318,32 @@ def test_config5_reconstruct_sampled_tokens():
     check(Kg[..., :128].double().numpy(), Kr[..., :128], BF16_TOL, "k_nope")
     check(Vg.double().numpy(), Vr, BF16_TOL, "v")
     assert torch.equal(host(K)[..., 128:], inp["k_rope"][:, None, :].expand(8192, 128, 64))
+
+
+# --------------------------------------------------------------------------
+# one GPU's tensor-parallel share: n_local_heads = 128 / G heads (the cache is
+# still read whole), with the YaRN-extended scale of the mla-init excerpt
+# --------------------------------------------------------------------------
+
+YARN = dict(qk_head_dim=192, max_seq_len=163840, original_seq_len=4096, mscale=1.0,
+            rope_factor=40.0)  # a test setting: the pages give no values
+
+
+@pytest.mark.parametrize("n_h,K", [(64, None), (32, None), (16, None), (96, None), (32, 300)])
+def test_tensor_parallel_share_full_step_with_yarn_scale(n_h, K):
+    scale = mla.mla_softmax_scale(**YARN)
+    assert abs(scale - oracle.softmax_scale(**YARN)) <= 2.0 ** -24 * scale
+    B, T = 4, 700
+    inp = synth.decode_inputs(B, n_h, T, torch.bfloat16, seed=n_h * 31 + T, topk=K)
+    topk = inp.get("topk_idx")
+    cache = cuda(inp["cache"])
+    w = cuda(inp["wkv_b"])
+    q_lat = mla.mla_absorb_q(cuda(inp["q_nope"]), w)
+    o_lat = mla.mla_decode_latent_attn(q_lat, cuda(inp["q_pe"]), cache[..., :512],
+                                       cache[..., 512:], scale=scale,
+                                       topk_idx=None if topk is None else cuda(topk))
+    out = mla.mla_out_up(o_lat, w)
+    c = inp["cache"]
+    ref = oracle.decode_absorbed(inp["q_nope"], inp["q_pe"], c[..., :512], c[..., 512:],
+                                 inp["wkv_b"], topk_idx=topk, scale=oracle.softmax_scale(**YARN))
+    check(f64(out), ref["out"], BF16_TOL, f"out n_h={n_h}")

@@ -415,3 +415,25 @@ def test_page_counts():
     assert cache.numel() * cache.element_size() == 2 * 33 * (512 + 64) * 2
     # the B=32, T=4096 decode workload: 32 x 4096 x 576 x 2 bytes
     assert 32 * 4096 * (512 + 64) * 2 == 150_994_944
+
+
+# --------------------------------------------------------------------------
+# attention scale ("Key–value latent", mla-init excerpt): closed forms
+# --------------------------------------------------------------------------
+
+def test_softmax_scale_closed_forms():
+    def near(a, b):  # the oracle takes 1/sqrt, Python's ** takes pow: within 2 ulp
+        return abs(a - b) <= 4.5e-16 * abs(b)
+    base = 192 ** -0.5
+    # no context extension: qk_head_dim^-1/2 with the 128 + 64 features
+    assert near(oracle.softmax_scale(192), base)
+    assert near(oracle.softmax_scale(192, max_seq_len=4096, original_seq_len=4096,
+                                     mscale=1.0, rope_factor=40.0), base)
+    # extension: factor (0.1 * m * ln(rope_factor) + 1)^2; ln(e^10) = 10 gives 2^2
+    assert near(oracle.softmax_scale(192, 163840, 4096, mscale=1.0, rope_factor=math.exp(10.0)),
+                4.0 * base)
+    # m = 0 switches the factor off; m = 0.5, ln = 10 gives 1.5^2
+    assert near(oracle.softmax_scale(192, 163840, 4096, 0.0, 40.0), base)
+    assert near(oracle.softmax_scale(192, 163840, 4096, 0.5, math.exp(10.0)), 2.25 * base)
+    assert math.isnan(oracle.softmax_scale(0))
+    assert math.isnan(oracle.softmax_scale(192, 2, 1, 1.0, 0.0))
