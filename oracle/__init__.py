@@ -18,6 +18,8 @@ Parity status (all pinned by ``tests/test_oracle_*.py``):
   decode_absorbed     pinned: equals decode_naive; closed forms
   decode_naive        pinned: torch scaled_dot_product_attention (double)
   kv_reconstruct      pinned: structured weights with a closed form
+  cache_append        pinned: RMSNorm closed forms (constant, scaled, unit
+                      RMS), rotation by quarter turns, composition, pairing
 """
 from __future__ import annotations
 
@@ -63,9 +65,10 @@ def _load():
                                          I, I, I, I, P, I, D, P, P]
         lib.orc_softmax_scale.argtypes = [I, L, L, D, D]
         lib.orc_softmax_scale.restype = D
+        lib.orc_cache_append.argtypes = [P, P, I, P, P, P, L, L, I, I, D, P, P]
         for name in ("orc_dequant_fp8_block", "orc_absorb_q", "orc_latent_attention",
                      "orc_out_up", "orc_decode_absorbed", "orc_kv_reconstruct",
-                     "orc_decode_naive"):
+                     "orc_decode_naive", "orc_cache_append"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -265,3 +268,24 @@ def softmax_scale(qk_head_dim=192, max_seq_len=0, original_seq_len=0, mscale=1.0
     max_seq_len > original_seq_len), in double."""
     return _load().orc_softmax_scale(qk_head_dim, max_seq_len, original_seq_len,
                                      float(mscale), float(rope_factor))
+
+
+def cache_append(kv, k_pe, gamma, freqs, pos, eps=1e-6):
+    """(latent rows [N,d_c], rotary rows [N,d_r]) in double: RMSNorm of the
+    latent with gain gamma, and the rotary key rotated pairwise by the table
+    row freqs[pos[n]] ((cos, sin) per pair)."""
+    x = np.ascontiguousarray(_np(kv))
+    r = np.ascontiguousarray(_np(k_pe))
+    assert x.dtype == r.dtype and x.shape[0] == r.shape[0]
+    g = np.ascontiguousarray(_np(gamma), dtype=np.float32)
+    f = np.ascontiguousarray(_np(freqs), dtype=np.float32)
+    p = np.ascontiguousarray(_np(pos), dtype=np.int32)
+    N, d_c = x.shape
+    d_r = r.shape[1]
+    assert g.shape == (d_c,) and f.shape[1:] == (d_r // 2, 2) and p.shape == (N,)
+    lat = np.empty((N, d_c), np.float64)
+    rope = np.empty((N, d_r), np.float64)
+    _check(_load().orc_cache_append(_ptr(x), _ptr(r), _dt(x), _ptr(g), _ptr(f), _ptr(p), N,
+                                    f.shape[0], d_c, d_r, float(eps), _ptr(lat), _ptr(rope)),
+           "cache_append")
+    return lat, rope

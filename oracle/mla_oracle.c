@@ -423,3 +423,54 @@ double orc_softmax_scale(int qk_head_dim, int64_t max_seq_len, int64_t original_
   }
   return scale;
 }
+
+/* ---- cache append ----------------------------------------------------------
+ * The new token's entries of the compressed cache. "DeepSeek-V3.2-Exp ·
+ * Key–value latent", section "Key–value down-projection" (mla-kv excerpt):
+ * the joint down-projection is split into the latent and the rotary key; the
+ * latent is normalised and the key rotated. Section "Key–value latent
+ * RMSNorm" (rmsnorm excerpt): in float32, var = mean of the squares over the
+ * feature axis, x * rsqrt(var + eps), times a per-feature gain, then cast
+ * back once. "DeepSeek V3" (inference notes), "Decoupled RoPE": the rotary
+ * key is computed once per token, shared by all heads and cached.
+ *
+ * Rotation reading (the pages show neither the body of the rotary helper nor
+ * its frequency table): features (2i, 2i+1) form a pair that is rotated by
+ * the angle of entry i of the table row for the token's position, given as
+ * (cos, sin) in freqs[pos][i][0..1]:
+ *   y[2i]   = x[2i] cos - x[2i+1] sin
+ *   y[2i+1] = x[2i] sin + x[2i+1] cos
+ * i.e. (x[2i] + i x[2i+1]) times the unit complex number (cos + i sin).
+ *
+ * kv [N, d_c], k_pe [N, d_r] (dt_in), gamma [d_c] f32, freqs [P, d_r/2, 2]
+ * f32, pos [N] int32 (each < P). Out: lat_out [N, d_c], rope_out [N, d_r]
+ * doubles (unrounded). Parity: pinned (closed forms for constant and scaled
+ * rows, unit RMS, quarter-turn and composed rotations, single-feature pairing).
+ */
+int orc_cache_append(const void* kv, const void* k_pe, int dt_in, const float* gamma,
+                     const float* freqs, const int32_t* pos, int64_t N, int64_t P,
+                     int d_c, int d_r, double eps, double* lat_out, double* rope_out) {
+  if (N < 0 || P < 0 || d_c <= 0 || d_r <= 0 || (d_r & 1) || eps < 0) return -1;
+  for (int64_t n = 0; n < N; n++)
+    if (pos[n] < 0 || pos[n] >= P) return -1;
+  for (int64_t n = 0; n < N; n++) {
+    double ss = 0.0;
+    for (int c = 0; c < d_c; c++) {
+      const double x = load(kv, n * d_c + c, dt_in);
+      ss += x * x;
+    }
+    const double var = ss / d_c;
+    const double inv = 1.0 / sqrt(var + eps);
+    for (int c = 0; c < d_c; c++)
+      lat_out[n * d_c + c] = (double)gamma[c] * (load(kv, n * d_c + c, dt_in) * inv);
+    const float* f = freqs + (int64_t)pos[n] * d_r;
+    for (int i = 0; i < d_r / 2; i++) {
+      const double x0 = load(k_pe, n * d_r + 2 * i, dt_in);
+      const double x1 = load(k_pe, n * d_r + 2 * i + 1, dt_in);
+      const double c = f[2 * i], s = f[2 * i + 1];
+      rope_out[n * d_r + 2 * i] = x0 * c - x1 * s;
+      rope_out[n * d_r + 2 * i + 1] = x0 * s + x1 * c;
+    }
+  }
+  return 0;
+}

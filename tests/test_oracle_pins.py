@@ -437,3 +437,110 @@ def test_softmax_scale_closed_forms():
     assert near(oracle.softmax_scale(192, 163840, 4096, 0.5, math.exp(10.0)), 2.25 * base)
     assert math.isnan(oracle.softmax_scale(0))
     assert math.isnan(oracle.softmax_scale(192, 2, 1, 1.0, 0.0))
+
+
+# --------------------------------------------------------------------------
+# cache append: RMSNorm of the latent and rotation of the rotary key
+# ("Key–value down-projection" and "Key–value latent RMSNorm" sections)
+# --------------------------------------------------------------------------
+
+def _angles_table(theta):
+    th = np.asarray(theta, np.float64)
+    return np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+
+
+def test_rmsnorm_constant_row_closed_form():
+    # x = c * ones: mean of squares is c^2, so y = gamma * c / sqrt(c^2 + eps)
+    d_c, d_r = 512, 64
+    for c, eps in ((0.75, 1e-6), (-3.0, 0.0), (1e-3, 1e-6), (2.0, 0.5)):
+        x = np.full((1, d_c), c, np.float32)
+        g = np.linspace(-2, 2, d_c).astype(np.float32)
+        lat, _ = oracle.cache_append(x, np.zeros((1, d_r), np.float32), g,
+                                     _angles_table(np.zeros((1, 32))), [0], eps=eps)
+        want = g.astype(np.float64) * (np.float64(np.float32(c)) /
+                                       math.sqrt(np.float64(np.float32(c)) ** 2 + eps))
+        np.testing.assert_allclose(lat[0], want, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_unit_rms_scale_invariance_and_zero_row():
+    g = rng(41)
+    x = g.standard_normal((4, 512)).astype(np.float32)
+    x[1] *= 1024.0  # scaling by a power of two is exact in float32
+    ones = np.ones(512, np.float32)
+    z = np.zeros((4, 64), np.float32)
+    tab = _angles_table(np.zeros((1, 32)))
+    lat, _ = oracle.cache_append(x, z, ones, tab, [0] * 4, eps=0.0)
+    np.testing.assert_allclose(np.sqrt((lat ** 2).mean(1)), 1.0, rtol=1e-14)
+    lat1, _ = oracle.cache_append(x[1:2] / 1024.0, z[:1], ones, tab, [0], eps=0.0)
+    np.testing.assert_allclose(lat[1], lat1[0], rtol=1e-14)
+    # the mean runs over all 512 features, not a sum and not 511 of them:
+    # a single nonzero feature v gives sqrt(512) * sign(v)
+    e = np.zeros((1, 512), np.float32)
+    e[0, 77] = -5.0
+    le, _ = oracle.cache_append(e, z[:1], ones, tab, [0], eps=0.0)
+    assert le[0, 77] == pytest.approx(-math.sqrt(512), rel=1e-15)
+    assert np.count_nonzero(le[0]) == 1
+    # eps keeps an all-zero row finite
+    l0, _ = oracle.cache_append(np.zeros((1, 512), np.float32), z[:1], ones, tab, [0])
+    assert np.all(l0 == 0.0)
+
+
+def test_rotation_pairing_quarter_turns_and_identity():
+    d_r = 64
+    tab = _angles_table(np.array([np.zeros(32), np.full(32, math.pi / 2),
+                                  np.full(32, math.pi)]))
+    # quarter-turn entries of the table, as float32, are not exactly (0, 1);
+    # the pins below use the table's own values
+    c1, s1 = np.float64(tab[1, 0, 0]), np.float64(tab[1, 0, 1])
+    ones = np.ones(512, np.float32)
+    lat0 = np.ones((1, 512), np.float32)
+    for k in (0, 5, 31):
+        x = np.zeros((1, d_r), np.float32)
+        x[0, 2 * k] = 1.0  # first feature of pair k only
+        _, r0 = oracle.cache_append(lat0, x, ones, tab, [0])
+        _, r1 = oracle.cache_append(lat0, x, ones, tab, [1])
+        assert np.array_equal(r0[0], x[0].astype(np.float64))  # angle 0: identity
+        want = np.zeros(d_r)
+        want[2 * k], want[2 * k + 1] = c1, s1  # (1, 0) turns to (cos, sin)
+        assert np.array_equal(r1[0], want)
+        y = np.zeros((1, d_r), np.float32)
+        y[0, 2 * k + 1] = 1.0  # (0, 1) turns to (-sin, cos)
+        _, r2 = oracle.cache_append(lat0, y, ones, tab, [1])
+        want = np.zeros(d_r)
+        want[2 * k], want[2 * k + 1] = -s1, c1
+        assert np.array_equal(r2[0], want)
+
+
+def test_rotation_preserves_pair_norms_and_composes():
+    g = rng(43)
+    N, d_r = 6, 64
+    x = g.standard_normal((N, d_r)).astype(np.float32)
+    a = g.uniform(-math.pi, math.pi, (N, 32))
+    b = g.uniform(-math.pi, math.pi, (N, 32))
+    lat = np.ones((N, 512), np.float32)
+    ones = np.ones(512, np.float32)
+    pos = np.arange(N, dtype=np.int32)
+    ta, tb, tab = _angles_table(a), _angles_table(b), _angles_table(a + b)
+    _, ra = oracle.cache_append(lat, x, ones, ta, pos)
+    n_in = np.hypot(x[:, 0::2].astype(np.float64), x[:, 1::2])
+    n_out = np.hypot(ra[:, 0::2], ra[:, 1::2])
+    # float32 cos/sin are within 2^-24 of a unit vector
+    np.testing.assert_allclose(n_out, n_in, rtol=2e-7)
+    # rotating by a, then by b, equals rotating by a + b (up to the float32
+    # rounding of the tables and of the intermediate result)
+    _, rab = oracle.cache_append(lat, ra.astype(np.float32), ones, tb, pos)
+    _, rs = oracle.cache_append(lat, x, ones, tab, pos)
+    np.testing.assert_allclose(rab, rs, atol=2e-6 * np.abs(x).max())
+    # and the table row is chosen by position, not by row number
+    _, rrev = oracle.cache_append(lat[::-1].copy(), x[::-1].copy(), ones, ta, pos[::-1].copy())
+    np.testing.assert_array_equal(rrev[::-1], ra)
+
+
+def test_cache_append_rejects_positions_outside_the_table():
+    lat = np.ones((2, 512), np.float32)
+    kp = np.ones((2, 64), np.float32)
+    tab = _angles_table(np.zeros((3, 32)))
+    with pytest.raises(ValueError):
+        oracle.cache_append(lat, kp, np.ones(512, np.float32), tab, [0, 3])
+    with pytest.raises(ValueError):
+        oracle.cache_append(lat, kp, np.ones(512, np.float32), tab, [-1, 0])
