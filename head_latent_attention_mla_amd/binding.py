@@ -58,8 +58,10 @@ def library() -> ctypes.CDLL:
         lib.mla_kv_reconstruct.argtypes = [P, P, P, P, P, L, I, I, P]
         lib.mla_softmax_scale.argtypes = [I, L, L, F, F]
         lib.mla_softmax_scale.restype = F
+        lib.mla_cache_append.argtypes = [P, L, P, F, P, I, P, P, L, P, P, L, L, L, L, I, I, I,
+                                         P]
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
-                     "mla_out_up", "mla_kv_reconstruct"):
+                     "mla_out_up", "mla_kv_reconstruct", "mla_cache_append"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -255,3 +257,41 @@ def mla_softmax_scale(qk_head_dim: int = 192, max_seq_len: int = 0, original_seq
     original_seq_len); see include/mla.h."""
     return library().mla_softmax_scale(qk_head_dim, max_seq_len, original_seq_len, mscale,
                                        rope_factor)
+
+
+def mla_cache_append(kv_a: torch.Tensor, gamma: torch.Tensor, freqs: torch.Tensor,
+                     pos: torch.Tensor, latent: torch.Tensor, rope: torch.Tensor,
+                     seq_idx: torch.Tensor = None, eps: float = 1e-6, stream=None):
+    """Write RMSNorm(kv_a[n, :512]) * gamma and the rotated kv_a[n, 512:576]
+    into latent[s, pos[n]] and rope[s, pos[n]] (s = seq_idx[n], or n).
+
+    kv_a [N, >=576] with unit stride in the last dim (the down-projection
+    output, latent features first); gamma [512] float32; freqs [n_pos, 32, 2]
+    float32 (cos, sin) per position and rotary pair; latent [B, T, 512] and
+    rope [B, T, 64] caches (views of a packed [B, T, 576] cache allowed).
+    Rows addressed outside the caches or the table are skipped. Returns
+    (latent, rope).
+    """
+    _dev(kv_a, gamma, freqs, pos, latent, rope, seq_idx)
+    _require(kv_a.dim() == 2 and kv_a.stride(1) == 1 and kv_a.shape[1] >= 576,
+             "kv_a must be [N, >=576] with unit stride in the last dim")
+    N = kv_a.shape[0]
+    _require(gamma.dtype == torch.float32 and gamma.is_contiguous() and
+             tuple(gamma.shape) == (512,), "gamma must be contiguous float32 [512]")
+    _require(freqs.dtype == torch.float32 and freqs.is_contiguous() and freqs.dim() == 3 and
+             tuple(freqs.shape[1:]) == (32, 2), "freqs must be contiguous float32 [n_pos, 32, 2]")
+    _require(pos.dtype == torch.int32 and pos.is_contiguous() and tuple(pos.shape) == (N,),
+             "pos must be contiguous int32 [N]")
+    if seq_idx is not None:
+        _require(seq_idx.dtype == torch.int32 and seq_idx.is_contiguous() and
+                 tuple(seq_idx.shape) == (N,), "seq_idx must be contiguous int32 [N]")
+    _require(latent.dtype == kv_a.dtype and rope.dtype == kv_a.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    B_cache = min(latent.shape[0], rope.shape[0])
+    T_cache = min(latent.shape[1], rope.shape[1])
+    _check("mla_cache_append", library().mla_cache_append(
+        _ptr(kv_a), kv_a.stride(0), _ptr(gamma), float(eps), _ptr(freqs), freqs.shape[0],
+        _ptr(seq_idx), _ptr(pos), N, _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B_cache,
+        T_cache, _dtype_code(kv_a), _stream(stream)))
+    return latent, rope

@@ -254,6 +254,39 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope, const void* wkv
                   "kv_reconstruct launch");
 }
 
+mla_status mla_cache_append(const void* kv_a, int64_t in_rstride, const float* gamma, float eps,
+                            const float* freqs, int n_pos, const int32_t* seq_idx,
+                            const int32_t* pos, int64_t N, void* latent, void* rope,
+                            int64_t lat_bstride, int64_t lat_rstride, int64_t rope_bstride,
+                            int64_t rope_rstride, int B_cache, int T_cache, mla_dtype dt,
+                            hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (N < 0 || n_pos < 0 || B_cache < 0 || T_cache < 0)
+    return fail(MLA_ERR_INVALID_ARG, "N=%lld n_pos=%d B_cache=%d T_cache=%d", (long long)N,
+                n_pos, B_cache, T_cache);
+  if (!(eps >= 0.f)) return fail(MLA_ERR_INVALID_ARG, "eps=%g is negative or NaN", (double)eps);
+  if (N == 0) return MLA_OK;
+  if (!kv_a || !gamma || !freqs || !pos || !latent || !rope)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!seq_idx && N > B_cache)
+    return fail(MLA_ERR_INVALID_ARG, "N=%lld rows without seq_idx but only %d sequences",
+                (long long)N, B_cache);
+  if (in_rstride < D_QK || lat_rstride < D_C || rope_rstride < D_R || lat_bstride < 0 ||
+      rope_bstride < 0)
+    return fail(MLA_ERR_INVALID_ARG, "stride too small");
+  const int64_t vec = dt == MLA_BF16 ? 8 : 4;
+  if (!aligned16(kv_a) || !aligned16(gamma) || !aligned16(freqs) || !aligned16(latent) ||
+      !aligned16(rope))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  if (in_rstride % vec || lat_rstride % vec || rope_rstride % vec || lat_bstride % vec ||
+      rope_bstride % vec)
+    return fail(MLA_ERR_UNSUPPORTED, "strides must be multiples of %lld elements", (long long)vec);
+  if ((N + 3) / 4 > INT_MAX) return fail(MLA_ERR_UNSUPPORTED, "N too large for one launch");
+  AppendParams p{kv_a, in_rstride, gamma, eps, freqs, n_pos, seq_idx, pos, N, latent, rope,
+                 lat_bstride, lat_rstride, rope_bstride, rope_rstride, B_cache, T_cache};
+  return from_hip(launch_cache_append(p, dt == MLA_BF16, stream), "cache_append launch");
+}
+
 }  // extern "C"
 
 extern "C" float mla_softmax_scale(int qk_head_dim, int64_t max_seq_len, int64_t original_seq_len,

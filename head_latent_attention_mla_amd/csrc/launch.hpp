@@ -40,4 +40,22 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream);
 
+struct AppendParams {
+  const void* kv_a;      // [N, in_rstride]: 512 latent then 64 rotary features
+  int64_t in_rstride;    // elements
+  const float* gamma;    // [512]
+  float eps;
+  const float* freqs;    // [n_pos, 32, 2] (cos, sin)
+  int n_pos;
+  const int32_t* seq_idx;  // [N] or nullptr (row n -> sequence n)
+  const int32_t* pos;      // [N]
+  int64_t N;
+  void* latent;
+  void* rope;
+  int64_t lat_bs, lat_rs, rope_bs, rope_rs;  // element strides
+  int B_cache, T_cache;
+};
+
+hipError_t launch_cache_append(const AppendParams& p, bool is_bf16, hipStream_t stream);
+
 }  // namespace mla

@@ -7,10 +7,11 @@ device or hand them to the oracle.
 
 Recipe (one numpy PCG64 stream per tensor, spawned from one SeedSequence,
 in the fixed order latent, rope, q_nope, q_pe, wkv_b, scales, top-k, then
-the stand-alone stage inputs q_lat and o_lat):
-  latent   rows ~ N(0,1) in float32, each row divided by its root mean square
-           (eps 1e-6, unit gain): the distribution of the normalised KV
-           latent that the cache holds.
+the stand-alone stage inputs q_lat and o_lat, then the cache-append inputs
+kv_a, gain, angles, positions):
+  latent   ~ N(0,1) in float32: the spread of the normalised KV latent the
+           cache holds (the root mean square of 512 standard normals is
+           1 +- 0.03; no normalisation is applied here).
   rope     ~ N(0,1)           (already-rotated shared key)
   q_nope   ~ N(0,1), q_pe ~ N(0,1)
   wkv_b    ~ N(0, 1/512)  [n_h*256, 512], stored [out, in]
@@ -20,6 +21,13 @@ the stand-alone stage inputs q_lat and o_lat):
            replacement from [0, T), unsorted
   q_lat    ~ N(0, 1/4)  (the spread of q_nope @ W^UK for the above)
   o_lat    ~ N(0, 1)
+  kv_a     down-projection output rows [N, 576] ~ N(0,1) times a per-row
+           scale 2^U[-2, 3] (unnormalised activations of varied size)
+  gain     RMSNorm gain [512] ~ U[0.5, 1.5]
+  angles   rotation table [n_pos, 32]: angles ~ U[-pi, pi), stored as
+           float32 (cos, sin) pairs
+  pos      per row: the sequence's current length, ~ U[0, T) (decode), or
+           consecutive positions (prefill)
 Values are rounded once to the storage type (bf16 round-to-nearest-even via
 torch, or kept float32).
 """
@@ -31,7 +39,8 @@ import torch
 D_C, D_R, D_N, D_V = 512, 64, 128, 128
 SCALE = 192 ** -0.5
 
-_ORDER = ("latent", "rope", "q_nope", "q_pe", "wkv_b", "scales", "topk", "q_lat", "o_lat")
+_ORDER = ("latent", "rope", "q_nope", "q_pe", "wkv_b", "scales", "topk", "q_lat", "o_lat",
+          "kv_a", "gain", "angles", "pos")
 
 
 def _streams(seed: int) -> dict:
@@ -44,11 +53,6 @@ def _normal(g, shape, std=1.0):
     if std != 1.0:
         x *= np.float32(std)
     return x
-
-
-def _unit_rms_rows(x: np.ndarray) -> np.ndarray:
-    ms = np.mean(x * x, axis=-1, keepdims=True, dtype=np.float32)
-    return (x / np.sqrt(ms + np.float32(1e-6))).astype(np.float32)
 
 
 def _store(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
@@ -72,7 +76,7 @@ def decode_inputs(B: int, n_h: int, T: int, dtype=torch.bfloat16, seed: int = 0,
     """
     g = _streams(seed)
     cache = np.empty((B, T, D_C + D_R), np.float32)
-    cache[..., :D_C] = _unit_rms_rows(_normal(g["latent"], (B, T, D_C)))
+    cache[..., :D_C] = _normal(g["latent"], (B, T, D_C))
     cache[..., D_C:] = _normal(g["rope"], (B, T, D_R))
     out = {
         "cache": _store(cache, dtype),
@@ -102,13 +106,47 @@ def decode_inputs(B: int, n_h: int, T: int, dtype=torch.bfloat16, seed: int = 0,
 
 
 def reconstruct_inputs(N: int, n_h: int, dtype=torch.bfloat16, seed: int = 0) -> dict:
-    """c [N, 512] (unit-RMS rows), k_rope [N, 64], wkv_b [n_h*256, 512]."""
+    """c [N, 512], k_rope [N, 64], wkv_b [n_h*256, 512]."""
     g = _streams(seed)
     return {
-        "c": _store(_unit_rms_rows(_normal(g["latent"], (N, D_C))), dtype),
+        "c": _store(_normal(g["latent"], (N, D_C)), dtype),
         "k_rope": _store(_normal(g["rope"], (N, D_R)), dtype),
         "wkv_b": _store(_normal(g["wkv_b"], (n_h * (D_N + D_V), D_C), std=512 ** -0.5), dtype),
     }
+
+
+def append_inputs(N: int, B: int, T: int, dtype=torch.bfloat16, seed: int = 0,
+                  prefill: bool = False, n_pos: int | None = None) -> dict:
+    """Inputs of one cache append.
+
+    Decode (prefill=False): N <= B rows, row n is the new token of sequence n
+    at position pos[n] ~ U[0, T). Prefill: N = B * (N // B) rows, sequence
+    n // (N // B), consecutive positions from a random start so that the
+    block fits in [0, T). Returns kv_a [N, 576] (dtype), gamma [512] f32,
+    freqs [n_pos, 32, 2] f32 (cos, sin), pos [N] int32 and, for prefill,
+    seq_idx [N] int32.
+    """
+    g = _streams(seed)
+    n_pos = T if n_pos is None else n_pos
+    scale = np.exp2(g["kv_a"].uniform(-2.0, 3.0, size=(N, 1))).astype(np.float32)
+    kv_a = _normal(g["kv_a"], (N, D_C + D_R)) * scale
+    theta = g["angles"].uniform(-np.pi, np.pi, size=(n_pos, D_R // 2))
+    freqs = np.stack([np.cos(theta), np.sin(theta)], -1).astype(np.float32)
+    out = {
+        "kv_a": _store(kv_a, dtype),
+        "gamma": torch.from_numpy(g["gain"].uniform(0.5, 1.5, size=D_C).astype(np.float32)),
+        "freqs": torch.from_numpy(np.ascontiguousarray(freqs)),
+    }
+    if prefill:
+        per = N // B
+        assert per * B == N and per <= T
+        start = g["pos"].integers(0, T - per + 1, size=B)
+        out["pos"] = torch.from_numpy((start[:, None] + np.arange(per)).reshape(-1).astype(np.int32))
+        out["seq_idx"] = torch.from_numpy(np.repeat(np.arange(B), per).astype(np.int32))
+    else:
+        assert N <= B
+        out["pos"] = torch.from_numpy(g["pos"].integers(0, T, size=N).astype(np.int32))
+    return out
 
 
 def fp8_codes(rows: int, cols: int, seed: int = 0, with_nan: bool = False) -> torch.Tensor:

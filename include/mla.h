@@ -184,6 +184,42 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope,
                               int n_h, mla_dtype dt, hipStream_t stream);
 
 /*
+ * Cache append: the new tokens' entries of the compressed cache ([KVL]
+ * "Key–value down-projection": the down-projection output is split into the
+ * latent and the rotary key, the latent is normalised and the key rotated;
+ * [KVL] "Key–value latent RMSNorm": float32 arithmetic, mean of squares,
+ * per-feature gain, one cast back; [DS3] "Decoupled RoPE": the rotated key is
+ * cached once per token and shared by all heads). For row n, with
+ * x = kv_a[n, 0:512], k = kv_a[n, 512:576], s = seq_idx[n] (or n when
+ * seq_idx is NULL), t = pos[n] and (cos_i, sin_i) = freqs[t, i, 0:2]:
+ *   latent(s,t,c)    = gamma[c] * (x[c] * rsqrt(mean_c x[c]^2 + eps))
+ *   rope(s,t,2i)     = k[2i] cos_i - k[2i+1] sin_i
+ *   rope(s,t,2i+1)   = k[2i] sin_i + k[2i+1] cos_i,     i < 32
+ * computed in fp32 and rounded once to dt. The rotation of consecutive
+ * feature pairs by a caller-supplied per-position angle table is this
+ * library's reading of the rotary step, whose body the pages do not show.
+ *   kv_a    [N, in_rstride] (dt): 576 used features per row.
+ *   gamma   [512] float32, freqs [n_pos, 32, 2] float32 (cos, sin).
+ *   seq_idx [N] int32 or NULL; pos [N] int32.
+ *   latent element (s,t,c) at latent[s*lat_bstride + t*lat_rstride + c],
+ *   rope   element (s,t,r) at rope  [s*rope_bstride + t*rope_rstride + r]
+ *          (dt; the layouts mla_decode_latent_attn reads, packed [.,576]
+ *          included).
+ * Rows whose (s, t) lies outside [0, B_cache) x [0, min(T_cache, n_pos))
+ * are skipped on the device (nothing is written for them). Two rows with
+ * the same (s, t) in one call race. Other cache rows are not touched.
+ * Requirements: in_rstride >= 576, lat_rstride >= 512, rope_rstride >= 64,
+ *   strides multiples of 8 (bf16) or 4 (f32) elements, eps >= 0;
+ *   N <= B_cache when seq_idx is NULL.
+ */
+mla_status mla_cache_append(const void* kv_a, int64_t in_rstride, const float* gamma, float eps,
+                            const float* freqs, int n_pos, const int32_t* seq_idx,
+                            const int32_t* pos, int64_t N, void* latent, void* rope,
+                            int64_t lat_bstride, int64_t lat_rstride, int64_t rope_bstride,
+                            int64_t rope_rstride, int B_cache, int T_cache, mla_dtype dt,
+                            hipStream_t stream);
+
+/*
  * mla_softmax_scale — the attention scale to pass as `scale` to
  * mla_decode_latent_attn ([KVL] mla-init excerpt): qk_head_dim^(-1/2)
  * (192 here: 128 content + 64 rotary features), and, when the model runs

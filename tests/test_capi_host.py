@@ -117,6 +117,35 @@ def test_reconstruct_argument_errors(lib):
     assert lib.mla_kv_reconstruct(None, None, None, None, None, 0, 16, BF16, s) == OK
 
 
+def append(lib, **kw):
+    a = dict(kv=FAKE, rs=576, gamma=FAKE, eps=1e-6, freqs=FAKE, n_pos=4096, seq=None, pos=FAKE,
+             N=8, lat=FAKE, rope=FAKE, lbs=4096 * 576, lrs=576, rbs=4096 * 576, rrs=576,
+             B=8, T=4096, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.mla_cache_append(a["kv"], a["rs"], a["gamma"], a["eps"], a["freqs"], a["n_pos"],
+                                a["seq"], a["pos"], a["N"], a["lat"], a["rope"], a["lbs"],
+                                a["lrs"], a["rbs"], a["rrs"], a["B"], a["T"], a["dt"],
+                                a["stream"])
+
+
+def test_cache_append_argument_errors(lib):
+    assert append(lib, kv=None) == INVALID
+    assert append(lib, pos=None) == INVALID
+    assert append(lib, gamma=None) == INVALID
+    assert append(lib, N=-1) == INVALID
+    assert append(lib, eps=-1.0) == INVALID
+    assert append(lib, eps=float("nan")) == INVALID
+    assert append(lib, rs=570) == INVALID                 # input row narrower than 576
+    assert append(lib, lrs=500) == INVALID
+    assert append(lib, rrs=32) == INVALID
+    assert append(lib, N=9) == INVALID                    # 9 rows, no seq_idx, 8 sequences
+    assert append(lib, rs=580) == UNSUPPORTED             # not a multiple of 8 elements
+    assert append(lib, rs=578, dt=F32) == UNSUPPORTED     # not a multiple of 4 elements
+    assert append(lib, freqs=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert append(lib, dt=3) == INVALID
+    assert append(lib, N=0, kv=None, pos=None) == OK      # no rows: no-op
+
+
 def test_binding_requires_device_tensors():
     import torch
     with pytest.raises(ValueError):
