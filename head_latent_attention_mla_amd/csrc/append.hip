@@ -13,8 +13,9 @@
 // with (cos_i, sin_i) = freqs[p][i] and (s, p) = (seq_idx[n], pos[n]).
 //
 // HBM-bound: per row 576 elements in, 576 out, plus 256 B of the rotation
-// table. One wave per row. For bf16 each lane reads 8 latent features (one
-// 16-byte load; the wave covers the 1 KB row in one instruction); for fp32
+// table. A wave handles a few rows, one row across its 64 lanes at a time.
+// For bf16 each lane reads 8 latent features of a row (one 16-byte load; the
+// wave covers the 1 KB row in one instruction); for fp32
 // two 16-byte loads 1 KB apart keep every instruction contiguous across the
 // wave. The sum of squares is reduced across the wave with lane shuffles.
 // Lanes 0..15 each also rotate two pairs of the rotary key.
@@ -25,7 +26,14 @@ namespace mla {
 
 namespace {
 
-constexpr int APPEND_ROWS_PER_BLOCK = 4;  // one 64-lane wave per row
+#ifndef MLA_APPEND_WAVES
+#define MLA_APPEND_WAVES 4
+#endif
+#ifndef MLA_APPEND_ROWS
+#define MLA_APPEND_ROWS 1
+#endif
+constexpr int APPEND_WAVES = MLA_APPEND_WAVES;  // waves per workgroup
+constexpr int APPEND_ROWS = MLA_APPEND_ROWS;    // rows per wave
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -75,61 +83,83 @@ __device__ __forceinline__ void store_lat(void* row, int lane, const float y[8])
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(64 * APPEND_ROWS_PER_BLOCK) void cache_append_kernel(AppendParams p) {
+// Each wave handles ROWS consecutive rows, all of their loads issued before
+// any arithmetic. One row per wave and four waves per workgroup measured
+// fastest on MI355X (within 11% of a plain device copy of the same bytes);
+// more rows per wave lower the occupancy more than they add bytes in flight.
+template <bool BF16, int ROWS>
+__global__ __launch_bounds__(64 * APPEND_WAVES) void cache_append_kernel(AppendParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * APPEND_ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (n >= p.N) return;
-  const int s = p.seq_idx ? p.seq_idx[n] : static_cast<int>(n);
-  const int t = p.pos[n];
-  // rows addressed outside the cache or the rotation table are not written
-  if (s < 0 || s >= p.B_cache || t < 0 || t >= p.T_cache || t >= p.n_pos) return;
+  const int64_t n0 =
+      (static_cast<int64_t>(blockIdx.x) * APPEND_WAVES + (threadIdx.x >> 6)) * ROWS;
   const int esz = BF16 ? 2 : 4;
-  const char* src = static_cast<const char*>(p.kv_a) + n * p.in_rstride * esz;
-
-  float x[8];
-  load_lat<BF16>(src, lane, x);
-  float ss = 0.f;
+  float x[ROWS][8], k4[ROWS][4];
+  floatx4 cs[ROWS];
+  int64_t dst_lat[ROWS], dst_rope[ROWS];
+  bool ok[ROWS];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ss += x[k] * x[k];
-  ss = wave_sum(ss);
-  // 1/512 is a power of two: the mean is exact in fp32
-  const float inv = rsqrtf(ss * (1.0f / D_C) + p.eps);
-  float y[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = p.gamma[lat_feature<BF16>(lane, k)] * (x[k] * inv);
-  char* dst = static_cast<char*>(p.latent) + (s * p.lat_bs + t * p.lat_rs) * esz;
-  store_lat<BF16>(dst, lane, y);
-
-  if (lane < D_R / 4) {  // 16 lanes x 4 rotary features (2 pairs)
-    float k4[4];
-    if constexpr (BF16) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(
-          reinterpret_cast<const uint16_t*>(src) + D_C + 4 * lane);
-      k4[0] = __uint_as_float(v[0] << 16);
-      k4[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-      k4[2] = __uint_as_float(v[1] << 16);
-      k4[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-    } else {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(
-          reinterpret_cast<const float*>(src) + D_C + 4 * lane);
-      for (int k = 0; k < 4; ++k) k4[k] = v[k];
+  for (int r = 0; r < ROWS; ++r) {
+    const int64_t n = n0 + r;
+    const bool in = n < p.N;
+    const int s = !in ? -1 : (p.seq_idx ? p.seq_idx[n] : static_cast<int>(n));
+    const int t = in ? p.pos[n] : -1;
+    // rows addressed outside the cache or the rotation table are not written
+    ok[r] = in && s >= 0 && s < p.B_cache && t >= 0 && t < p.T_cache && t < p.n_pos;
+    dst_lat[r] = s * p.lat_bs + t * p.lat_rs;
+    dst_rope[r] = s * p.rope_bs + t * p.rope_rs;
+    if (ok[r]) {
+      const char* src = static_cast<const char*>(p.kv_a) + n * p.in_rstride * esz;
+      load_lat<BF16>(src, lane, x[r]);
+      if (lane < D_R / 4) {  // 16 lanes x 4 rotary features (2 pairs)
+        if constexpr (BF16) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(
+              reinterpret_cast<const uint16_t*>(src) + D_C + 4 * lane);
+          k4[r][0] = __uint_as_float(v[0] << 16);
+          k4[r][1] = __uint_as_float(v[0] & 0xFFFF0000u);
+          k4[r][2] = __uint_as_float(v[1] << 16);
+          k4[r][3] = __uint_as_float(v[1] & 0xFFFF0000u);
+        } else {
+          const floatx4 v = *reinterpret_cast<const floatx4*>(
+              reinterpret_cast<const float*>(src) + D_C + 4 * lane);
+          for (int k = 0; k < 4; ++k) k4[r][k] = v[k];
+        }
+        // (cos, sin) of pairs 2*lane and 2*lane + 1
+        cs[r] = *reinterpret_cast<const floatx4*>(p.freqs + static_cast<int64_t>(t) * D_R +
+                                                  4 * lane);
+      }
     }
-    // (cos, sin) of pairs 2*lane and 2*lane + 1
-    const floatx4 cs =
-        *reinterpret_cast<const floatx4*>(p.freqs + static_cast<int64_t>(t) * D_R + 4 * lane);
-    float r[4];
-    r[0] = k4[0] * cs[0] - k4[1] * cs[1];
-    r[1] = k4[0] * cs[1] + k4[1] * cs[0];
-    r[2] = k4[2] * cs[2] - k4[3] * cs[3];
-    r[3] = k4[2] * cs[3] + k4[3] * cs[2];
-    char* rdst = static_cast<char*>(p.rope) + (s * p.rope_bs + t * p.rope_rs) * esz;
-    if constexpr (BF16) {
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(rdst) + 4 * lane) =
-          u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-    } else {
-      *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(rdst) + 4 * lane) =
-          floatx4{r[0], r[1], r[2], r[3]};
+  }
+  float g[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) g[k] = p.gamma[lat_feature<BF16>(lane, k)];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (!ok[r]) continue;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss += x[r][k] * x[r][k];
+    ss = wave_sum(ss);
+    // 1/512 is a power of two: the mean is exact in fp32
+    const float inv = rsqrtf(ss * (1.0f / D_C) + p.eps);
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = g[k] * (x[r][k] * inv);
+    store_lat<BF16>(static_cast<char*>(p.latent) + dst_lat[r] * esz, lane, y);
+    if (lane < D_R / 4) {
+      const float* kk = k4[r];
+      const floatx4 c = cs[r];
+      const float o0 = kk[0] * c[0] - kk[1] * c[1];
+      const float o1 = kk[0] * c[1] + kk[1] * c[0];
+      const float o2 = kk[2] * c[2] - kk[3] * c[3];
+      const float o3 = kk[2] * c[3] + kk[3] * c[2];
+      char* rdst = static_cast<char*>(p.rope) + dst_rope[r] * esz;
+      if constexpr (BF16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(rdst) + 4 * lane) =
+            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      } else {
+        *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(rdst) + 4 * lane) =
+            floatx4{o0, o1, o2, o3};
+      }
     }
   }
 }
@@ -137,10 +167,12 @@ __global__ __launch_bounds__(64 * APPEND_ROWS_PER_BLOCK) void cache_append_kerne
 }  // namespace
 
 hipError_t launch_cache_append(const AppendParams& p, bool is_bf16, hipStream_t stream) {
-  const int64_t blocks = (p.N + APPEND_ROWS_PER_BLOCK - 1) / APPEND_ROWS_PER_BLOCK;
-  auto kern = is_bf16 ? cache_append_kernel<true> : cache_append_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * APPEND_ROWS_PER_BLOCK),
-                     0, stream, p);
+  constexpr int per_block = APPEND_WAVES * APPEND_ROWS;
+  const int64_t blocks = (p.N + per_block - 1) / per_block;
+  auto kern = is_bf16 ? cache_append_kernel<true, APPEND_ROWS>
+                      : cache_append_kernel<false, APPEND_ROWS>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * APPEND_WAVES), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
