@@ -18,6 +18,8 @@ Parity status (all pinned by ``tests/test_oracle_*.py``):
   decode_absorbed     pinned: equals decode_naive; closed forms
   decode_naive        pinned: torch scaled_dot_product_attention (double)
   kv_reconstruct      pinned: structured weights with a closed form
+  latent_attention_multi  pinned: s_q = 1 case, per-token reduction to
+                      latent_attention (causal prefix / full), hand corner
   cache_append        pinned: RMSNorm closed forms (constant, scaled, unit
                       RMS), rotation by quarter turns, composition, pairing
 """
@@ -65,10 +67,13 @@ def _load():
                                          I, I, I, I, P, I, D, P, P]
         lib.orc_softmax_scale.argtypes = [I, L, L, D, D]
         lib.orc_softmax_scale.restype = D
+        lib.orc_latent_attention_multi.argtypes = [P, I, P, I, P, P, I, L, L, L, L, I, I, I,
+                                                   I, I, I, P, I, I, D, P, P]
         lib.orc_cache_append.argtypes = [P, P, I, P, P, P, L, L, I, I, D, P, P]
         for name in ("orc_dequant_fp8_block", "orc_absorb_q", "orc_latent_attention",
                      "orc_out_up", "orc_decode_absorbed", "orc_kv_reconstruct",
-                     "orc_decode_naive", "orc_cache_append"):
+                     "orc_decode_naive", "orc_cache_append",
+                     "orc_latent_attention_multi"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -198,6 +203,28 @@ def latent_attention(q_lat, q_pe, latent, rope, T=None, topk_idx=None, scale=192
                                         d_c, d_r, _ptr(idx), K, float(scale), _ptr(o),
                                         _ptr(lse), _ptr(probs)), "latent_attention")
     return o, lse, probs
+
+
+def latent_attention_multi(q_lat, q_pe, latent, rope, T=None, topk_idx=None,
+                           scale=192 ** -0.5, causal=False):
+    """Several query tokens per sequence: q_lat [B,s_q,n_h,d_c], q_pe
+    [B,s_q,n_h,d_r]; T counts the cached positions including the s_q new
+    tokens. Returns (out_lat [B,s_q,n_h,d_c], lse [B,s_q,n_h])."""
+    ql = np.ascontiguousarray(_np(q_lat))
+    qp = np.ascontiguousarray(_np(q_pe))
+    lat, rp, lbs, lrs, rbs, rrs = _cache_args(latent, rope)
+    B, s_q, n_h, d_c = ql.shape
+    d_r = qp.shape[3]
+    T = lat.shape[1] if T is None else T
+    idx, K = _idx_args(topk_idx, B)
+    o = np.empty((B, s_q, n_h, d_c), np.float64)
+    lse = np.empty((B, s_q, n_h), np.float64)
+    _check(_load().orc_latent_attention_multi(_ptr(ql), _dt(ql), _ptr(qp), _dt(qp), _ptr(lat),
+                                              _ptr(rp), _dt(lat), lbs, lrs, rbs, rrs, B, s_q,
+                                              n_h, T, d_c, d_r, _ptr(idx), K, int(causal),
+                                              float(scale), _ptr(o), _ptr(lse)),
+           "latent_attention_multi")
+    return o, lse
 
 
 def decode_absorbed(q_nope, q_pe, latent, rope, w, T=None, topk_idx=None,

@@ -246,6 +246,94 @@ int orc_latent_attention(const void* q_lat, int dt_ql, const void* q_pe, int dt_
   return bad ? -2 : 0;
 }
 
+/* ---- latent attention with several query tokens per sequence ---------------
+ * The same equation with the query-token axis s that the "Absorb key weights"
+ * decode excerpt carries in its einsums (q [b,s,h,c] against the cache
+ * [b,t,c], scores [b,s,h,t]): for sequence b, token j < s_q and head h,
+ *   z[t] = scale * ( q_lat[b,j,h,:] . latent[b,t,:] + q_pe[b,j,h,:] . rope[b,t,:] )
+ * over t < T, where T counts the cached positions including the s_q new
+ * tokens (they occupy positions T - s_q .. T - 1). The index set, when
+ * given, is one per sequence, shared by every token and head (the excerpt's
+ * mask has a singleton token axis). With causal != 0, token j also may not
+ * see positions after its own: t <= T - s_q + j (the reading of the causal
+ * mask of the prefill excerpt, "Value up-projection", for queries that sit
+ * at the end of the cache). p = softmax(z); out_lat[b,j,h,:] = sum_t p[t]
+ * latent[b,t,:]; lse[b,j,h] = log sum_t exp z[t]. Layouts [B, s_q, n_h, .].
+ * Parity: pinned (s_q = 1 is the single-token function; token j equals the
+ * single-token function over the first T - s_q + j + 1 positions when causal,
+ * over all T otherwise; hand-checked causal corner). */
+int orc_latent_attention_multi(const void* q_lat, int dt_ql, const void* q_pe, int dt_qp,
+                               const void* latent, const void* rope, int dt_cache,
+                               int64_t lat_bs, int64_t lat_rs, int64_t rope_bs,
+                               int64_t rope_rs, int B, int s_q, int n_h, int T, int d_c,
+                               int d_r, const int32_t* idx, int K, int causal, double scale,
+                               double* out_lat, double* lse) {
+  if (B < 0 || s_q < 1 || n_h < 1 || T < 1 || d_c < 1 || d_r < 0) return -1;
+  if (idx && (K < 1 || K > T)) return -1;
+  if (causal && T < s_q) return -1;
+  unsigned char* allowed = (unsigned char*)malloc((size_t)B * T);
+  if (!allowed) return -2;
+  for (int b = 0; b < B; b++)
+    if (build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, allowed + (int64_t)b * T)) {
+      free(allowed);
+      return -1;
+    }
+  int bad = 0;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+  for (int b = 0; b < B; b++)
+    for (int j = 0; j < s_q; j++)
+      for (int h = 0; h < n_h; h++) {
+        unsigned char* al = (unsigned char*)malloc((size_t)T);
+        double* z = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!al || !z) {
+#pragma omp atomic write
+          bad = 1;
+          free(al);
+          free(z);
+          continue;
+        }
+        for (int t = 0; t < T; t++)
+          al[t] = allowed[(int64_t)b * T + t] && !(causal && t > T - s_q + j);
+        int any = 0;
+        for (int t = 0; t < T; t++) any |= al[t];
+        int64_t qrow = ((int64_t)b * s_q + j) * n_h + h;
+        if (!any) { /* nothing visible: empty sum, zero output, lse = -inf */
+          for (int c = 0; c < d_c; c++) out_lat[qrow * d_c + c] = 0.0;
+          if (lse) lse[qrow] = -INFINITY;
+          free(al);
+          free(z);
+          continue;
+        }
+        for (int t = 0; t < T; t++) {
+          if (!al[t]) {
+            z[t] = -INFINITY;
+            continue;
+          }
+          int64_t lbase = (int64_t)b * lat_bs + (int64_t)t * lat_rs;
+          int64_t rbase = (int64_t)b * rope_bs + (int64_t)t * rope_rs;
+          double content = 0.0, rotary = 0.0;
+          for (int c = 0; c < d_c; c++)
+            content += load(q_lat, qrow * d_c + c, dt_ql) * load(latent, lbase + c, dt_cache);
+          for (int r = 0; r < d_r; r++)
+            rotary += load(q_pe, qrow * d_r + r, dt_qp) * load(rope, rbase + r, dt_cache);
+          z[t] = scale * (content + rotary);
+        }
+        double l = softmax_inplace(z, al, T);
+        if (lse) lse[qrow] = l;
+        for (int c = 0; c < d_c; c++) {
+          double acc = 0.0;
+          for (int t = 0; t < T; t++)
+            if (al[t])
+              acc += z[t] * load(latent, (int64_t)b * lat_bs + (int64_t)t * lat_rs + c, dt_cache);
+          out_lat[qrow * d_c + c] = acc;
+        }
+        free(al);
+        free(z);
+      }
+  free(allowed);
+  return bad ? -2 : 0;
+}
+
 /* ---- W^UV after the sum ----------------------------------------------------- */
 
 /* out[b,h,d] = sum_c o_lat[b,h,c] * W[h*(d_n+d_v) + d_n + d, c]

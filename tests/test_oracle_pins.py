@@ -544,3 +544,73 @@ def test_cache_append_rejects_positions_outside_the_table():
         oracle.cache_append(lat, kp, np.ones(512, np.float32), tab, [0, 3])
     with pytest.raises(ValueError):
         oracle.cache_append(lat, kp, np.ones(512, np.float32), tab, [-1, 0])
+
+
+# --------------------------------------------------------------------------
+# several query tokens per sequence (the token axis of the decode einsums)
+# --------------------------------------------------------------------------
+
+def _multi_problem(seed, B, s_q, n_h, T, d_c=16, d_r=4):
+    g = rng(seed)
+    return dict(q_lat=g.standard_normal((B, s_q, n_h, d_c)),
+                q_pe=g.standard_normal((B, s_q, n_h, d_r)),
+                latent=g.standard_normal((B, T, d_c)), rope=g.standard_normal((B, T, d_r)))
+
+
+def test_multi_token_with_one_token_is_the_single_token_function():
+    p = _multi_problem(51, 3, 1, 4, 37)
+    idx = np.stack([rng(52 + b).choice(37, 9, replace=False) for b in range(3)]).astype(np.int32)
+    for topk in (None, idx):
+        for causal in (False, True):
+            o, lse = oracle.latent_attention_multi(p["q_lat"], p["q_pe"], p["latent"], p["rope"],
+                                                   topk_idx=topk, scale=0.4, causal=causal)
+            o1, l1, _ = oracle.latent_attention(p["q_lat"][:, 0], p["q_pe"][:, 0], p["latent"],
+                                                p["rope"], topk_idx=topk, scale=0.4,
+                                                want_lse=True)
+            np.testing.assert_allclose(o[:, 0], o1, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(lse[:, 0], l1, rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_token_reduces_to_single_token_over_its_visible_prefix(causal):
+    B, s_q, n_h, T = 2, 5, 3, 23
+    p = _multi_problem(53, B, s_q, n_h, T)
+    o, lse = oracle.latent_attention_multi(p["q_lat"], p["q_pe"], p["latent"], p["rope"],
+                                           scale=0.3, causal=causal)
+    for j in range(s_q):
+        Tj = T - s_q + j + 1 if causal else T
+        oj, lj, _ = oracle.latent_attention(p["q_lat"][:, j], p["q_pe"][:, j], p["latent"],
+                                            p["rope"], T=Tj, scale=0.3, want_lse=True)
+        np.testing.assert_allclose(o[:, j], oj, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[:, j], lj, rtol=1e-12)
+    if causal:  # the last token sees everything, the first one does not
+        full, _, _ = oracle.latent_attention(p["q_lat"][:, 0], p["q_pe"][:, 0], p["latent"],
+                                             p["rope"], scale=0.3)
+        assert np.max(np.abs(o[:, 0] - full)) > 1e-6
+
+
+def test_causal_corner_first_token_of_a_full_block_sees_one_position():
+    # T == s_q: token 0 sits at position 0 and may only see it, so its output
+    # is that latent row and its lse is its own score
+    B, s_q, n_h, T = 2, 4, 3, 4
+    p = _multi_problem(55, B, s_q, n_h, T)
+    o, lse = oracle.latent_attention_multi(p["q_lat"], p["q_pe"], p["latent"], p["rope"],
+                                           scale=0.7, causal=True)
+    for b in range(B):
+        for h in range(n_h):
+            np.testing.assert_allclose(o[b, 0, h], p["latent"][b, 0], rtol=1e-14)
+            z = 0.7 * (p["q_lat"][b, 0, h] @ p["latent"][b, 0] + p["q_pe"][b, 0, h] @ p["rope"][b, 0])
+            assert lse[b, 0, h] == pytest.approx(z, rel=1e-13, abs=1e-13)
+
+
+def test_causal_with_an_index_set_that_hides_every_visible_row():
+    # the index set holds only the last position: the first token sees none of
+    # it (empty sum: zero output, lse -inf), the last token sees only it
+    B, s_q, n_h, T = 1, 3, 2, 10
+    p = _multi_problem(57, B, s_q, n_h, T)
+    idx = np.array([[T - 1]], np.int32)
+    o, lse = oracle.latent_attention_multi(p["q_lat"], p["q_pe"], p["latent"], p["rope"],
+                                           topk_idx=idx, causal=True)
+    assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(lse[0, 0]))
+    np.testing.assert_allclose(o[0, 2], np.broadcast_to(p["latent"][0, T - 1], (n_h, 16)),
+                               rtol=1e-14)
