@@ -58,10 +58,17 @@ def library() -> ctypes.CDLL:
         lib.mla_kv_reconstruct.argtypes = [P, P, P, P, P, L, I, I, P]
         lib.mla_softmax_scale.argtypes = [I, L, L, F, F]
         lib.mla_softmax_scale.restype = F
+        lib.mla_decode_latent_attn_multi.argtypes = [P, P, P, P, L, L, L, L, I, I, I, I, P, I,
+                                                     I, F, I, P, P, P, Z, I, P]
+        lib.mla_decode_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.mla_decode_step_workspace_bytes.restype = Z
+        lib.mla_decode_step.argtypes = [P, P, P, P, P, L, L, L, L, I, I, I, I, P, I, I, F, I, P,
+                                        P, P, Z, I, P]
         lib.mla_cache_append.argtypes = [P, L, P, F, P, I, P, P, L, P, P, L, L, L, L, I, I, I,
                                          P]
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
-                     "mla_out_up", "mla_kv_reconstruct", "mla_cache_append"):
+                     "mla_out_up", "mla_kv_reconstruct", "mla_cache_append",
+                     "mla_decode_latent_attn_multi", "mla_decode_step"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -206,6 +213,120 @@ def mla_decode_latent_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, latent: torc
         _ptr(topk_idx), K, float(scale), num_splits, _ptr(out_lat), _ptr(lse),
         _ptr(workspace), ws_bytes, _dtype_code(q_lat), _stream(stream)))
     return (out_lat, lse) if (want_lse or lse is not None) else out_lat
+
+
+def _topk_arg(topk_idx, B):
+    if topk_idx is None:
+        return 0
+    _require(topk_idx.dtype == torch.int32 and topk_idx.is_contiguous() and
+             topk_idx.dim() == 2 and topk_idx.shape[0] == B,
+             "topk_idx must be contiguous int32 [B, K]")
+    return topk_idx.shape[1]
+
+
+def mla_decode_latent_attn_multi(q_lat: torch.Tensor, q_pe: torch.Tensor, latent: torch.Tensor,
+                                 rope: torch.Tensor, T: int = None, topk_idx: torch.Tensor = None,
+                                 causal: bool = False, scale: float = SCALE, num_splits: int = 0,
+                                 out_lat: torch.Tensor = None, lse: torch.Tensor = None,
+                                 workspace: torch.Tensor = None, want_lse: bool = False,
+                                 stream=None):
+    """Latent attention of S_q query tokens per sequence: q_lat [B, S_q, n_h,
+    512], q_pe [B, S_q, n_h, 64]; T counts the cached positions including the
+    S_q new ones (default: the cache length). causal: token j sees positions
+    up to T - S_q + j. Returns out_lat [B, S_q, n_h, 512] (and lse
+    [B, S_q, n_h] fp32 if requested)."""
+    _dev(q_lat, q_pe, latent, rope, topk_idx, out_lat, lse, workspace)
+    _require(q_lat.dim() == 4 and q_lat.shape[3] == 512 and q_lat.is_contiguous(),
+             "q_lat must be contiguous [B, S_q, n_h, 512]")
+    B, S_q, n_h, _ = q_lat.shape
+    _require(q_pe.dtype == q_lat.dtype and q_pe.is_contiguous() and
+             tuple(q_pe.shape) == (B, S_q, n_h, 64), "q_pe must be contiguous [B, S_q, n_h, 64]")
+    _require(latent.dtype == q_lat.dtype and rope.dtype == q_lat.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    _require(latent.shape[0] >= B and rope.shape[0] >= B, "cache batch too small")
+    if T is None:
+        T = latent.shape[1]
+    _require(T <= latent.shape[1] and T <= rope.shape[1], "T exceeds the cache length")
+    K = _topk_arg(topk_idx, B)
+    if out_lat is None:
+        out_lat = torch.empty((B, S_q, n_h, 512), dtype=q_lat.dtype, device=q_lat.device)
+    _require(out_lat.dtype == q_lat.dtype and out_lat.is_contiguous() and
+             tuple(out_lat.shape) == (B, S_q, n_h, 512),
+             "out_lat must be contiguous [B, S_q, n_h, 512]")
+    if lse is None and want_lse:
+        lse = torch.empty((B, S_q, n_h), dtype=torch.float32, device=q_lat.device)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and
+                 tuple(lse.shape) == (B, S_q, n_h), "lse must be contiguous float32 [B, S_q, n_h]")
+    need = (mla_decode_workspace_bytes(B, S_q * n_h, T, K, num_splits, q_lat.dtype)
+            if B > 0 else 0)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_latent_attn_multi", library().mla_decode_latent_attn_multi(
+        _ptr(q_lat), _ptr(q_pe), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B, S_q, n_h, T,
+        _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out_lat), _ptr(lse),
+        _ptr(workspace), ws_bytes, _dtype_code(q_lat), _stream(stream)))
+    return (out_lat, lse) if (want_lse or lse is not None) else out_lat
+
+
+def mla_decode_step_workspace_bytes(B: int, S_q: int, n_h: int, T: int, K: int = 0,
+                                    num_splits: int = 0, dtype=torch.bfloat16) -> int:
+    code = MLA_BF16 if dtype == torch.bfloat16 else MLA_F32
+    v = library().mla_decode_step_workspace_bytes(B, S_q, n_h, T, K, num_splits, code)
+    if v == ctypes.c_size_t(-1).value:
+        raise MLAError("mla_decode_step_workspace_bytes", 1, "arguments rejected")
+    return v
+
+
+def mla_decode_step(q_nope: torch.Tensor, q_pe: torch.Tensor, wkv_b: torch.Tensor,
+                    latent: torch.Tensor, rope: torch.Tensor, T: int = None,
+                    topk_idx: torch.Tensor = None, causal: bool = False, scale: float = SCALE,
+                    num_splits: int = 0, out: torch.Tensor = None, lse: torch.Tensor = None,
+                    workspace: torch.Tensor = None, want_lse: bool = False, stream=None):
+    """The whole absorbed decode step in one call: q_nope [B, S_q, n_h, 128]
+    (or [B, n_h, 128] for one token), q_pe likewise with 64 features, wkv_b
+    [n_h*256, 512]. Returns out [B, S_q, n_h, 128] (the input's rank) and lse
+    if requested."""
+    _dev(q_nope, q_pe, wkv_b, latent, rope, topk_idx, out, lse, workspace)
+    squeeze = q_nope.dim() == 3
+    if squeeze:
+        q_nope, q_pe = q_nope.unsqueeze(1), q_pe.unsqueeze(1)
+    _require(q_nope.dim() == 4 and q_nope.shape[3] == 128 and q_nope.is_contiguous(),
+             "q_nope must be contiguous [B, S_q, n_h, 128]")
+    B, S_q, n_h, _ = q_nope.shape
+    _require(q_pe.dtype == q_nope.dtype and q_pe.is_contiguous() and
+             tuple(q_pe.shape) == (B, S_q, n_h, 64), "q_pe must be contiguous [B, S_q, n_h, 64]")
+    _require(wkv_b.dtype == q_nope.dtype and wkv_b.is_contiguous() and
+             tuple(wkv_b.shape) == (n_h * 256, 512), "wkv_b must be contiguous [n_h*256, 512]")
+    _require(latent.dtype == q_nope.dtype and rope.dtype == q_nope.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    _require(latent.shape[0] >= B and rope.shape[0] >= B, "cache batch too small")
+    if T is None:
+        T = latent.shape[1]
+    _require(T <= latent.shape[1] and T <= rope.shape[1], "T exceeds the cache length")
+    K = _topk_arg(topk_idx, B)
+    shape = (B, n_h, 128) if squeeze else (B, S_q, n_h, 128)
+    if out is None:
+        out = torch.empty(shape, dtype=q_nope.dtype, device=q_nope.device)
+    _require(out.dtype == q_nope.dtype and out.is_contiguous() and tuple(out.shape) == shape,
+             f"out must be contiguous {list(shape)}")
+    if lse is None and want_lse:
+        lse = torch.empty(shape[:-1], dtype=torch.float32, device=q_nope.device)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * S_q * n_h,
+                 "lse must be contiguous float32 with B * S_q * n_h elements")
+    if workspace is None and B > 0:
+        need = mla_decode_step_workspace_bytes(B, S_q, n_h, T, K, num_splits, q_nope.dtype)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_step", library().mla_decode_step(
+        _ptr(q_nope), _ptr(q_pe), _ptr(wkv_b), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B,
+        S_q, n_h, T, _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out),
+        _ptr(lse), _ptr(workspace), ws_bytes, _dtype_code(q_nope), _stream(stream)))
+    return (out, lse) if (want_lse or lse is not None) else out
 
 
 def mla_out_up(out_lat: torch.Tensor, wkv_b: torch.Tensor, out: torch.Tensor = None,

@@ -148,19 +148,39 @@ size_t mla_decode_workspace_bytes(int B, int n_h, int T, int K, int num_splits, 
   return ws_bytes_for(B, n_h, sp, dt);
 }
 
-mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const void* latent,
-                                  const void* rope, int64_t lat_bstride, int64_t lat_rstride,
-                                  int64_t rope_bstride, int64_t rope_rstride, int B, int n_h,
-                                  int T, const int32_t* topk_idx, int K, float scale,
-                                  int num_splits, void* out_lat, float* lse, void* workspace,
-                                  size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks and launch parameters shared by the decode calls: S_q
+// query tokens of n_h_tok heads per sequence, read as S_q * n_h_tok query
+// rows. *empty is set when there is nothing to launch (B == 0).
+mla_status decode_prepare(const void* q_lat, const void* q_pe, const void* latent,
+                          const void* rope, int64_t lat_bstride, int64_t lat_rstride,
+                          int64_t rope_bstride, int64_t rope_rstride, int B, int S_q,
+                          int n_h_tok, int T, const int32_t* topk_idx, int K, int causal,
+                          float scale, int num_splits, void* out_lat, float* lse,
+                          void* workspace, size_t ws_bytes, mla_dtype dt, DecodeParams* pp,
+                          bool* empty) {
+  *empty = false;
   if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (S_q < 1) return fail(MLA_ERR_INVALID_ARG, "S_q=%d < 1", S_q);
   const bool sparse = topk_idx != nullptr;
   int rows;
-  mla_status st = check_decode_dims(B, n_h, T, K, sparse, &rows);
+  mla_status st = check_decode_dims(B, n_h_tok, T, K, sparse, &rows);
   if (st != MLA_OK) return st;
-  if (B == 0) return MLA_OK;
-  if (B > 65535 || n_h > 65535) return fail(MLA_ERR_UNSUPPORTED, "B or n_h above 65535");
+  if (causal && T < S_q)
+    return fail(MLA_ERR_INVALID_ARG, "causal with T=%d < S_q=%d query tokens", T, S_q);
+  if (causal && sparse)
+    return fail(MLA_ERR_UNSUPPORTED, "the causal limit is implemented for dense attention only");
+  if (static_cast<int64_t>(S_q) * n_h_tok > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "S_q * n_h above 65535");
+  const int n_h = S_q * n_h_tok;  // query rows per sequence
+  if (B == 0) {
+    *empty = true;
+    return MLA_OK;
+  }
+  if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "B above 65535");
   if (!q_lat || !q_pe || !latent || !rope || !out_lat)
     return fail(MLA_ERR_INVALID_ARG, "null pointer");
   if (num_splits < 0) return fail(MLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
@@ -199,7 +219,8 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
                 workspace ? ws_bytes : static_cast<size_t>(0));
   if (need > 0 && !aligned16(workspace)) return fail(MLA_ERR_UNSUPPORTED, "misaligned workspace");
 
-  DecodeParams p{};
+  DecodeParams& p = *pp;
+  p = DecodeParams{};
   p.q_lat = q_lat;
   p.q_pe = q_pe;
   p.latent = latent;
@@ -211,6 +232,9 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
   p.B = B;
   p.n_h = n_h;
   p.T = T;
+  p.s_q = S_q;
+  p.n_h_tok = n_h_tok;
+  p.causal = causal ? 1 : 0;
   p.idx = topk_idx;
   p.K = sparse ? K : 0;
   p.rows = rows;
@@ -225,7 +249,115 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const voi
     p.ws_o = workspace;
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(bh * D_C * esz));
   }
+  return MLA_OK;
+}
+
+mla_status decode_impl(const void* q_lat, const void* q_pe, const void* latent, const void* rope,
+                       int64_t lat_bstride, int64_t lat_rstride, int64_t rope_bstride,
+                       int64_t rope_rstride, int B, int S_q, int n_h_tok, int T,
+                       const int32_t* topk_idx, int K, int causal, float scale, int num_splits,
+                       void* out_lat, float* lse, void* workspace, size_t ws_bytes,
+                       mla_dtype dt, hipStream_t stream) {
+  DecodeParams p;
+  bool empty;
+  mla_status st = decode_prepare(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride,
+                                 rope_bstride, rope_rstride, B, S_q, n_h_tok, T, topk_idx, K,
+                                 causal, scale, num_splits, out_lat, lse, workspace, ws_bytes, dt,
+                                 &p, &empty);
+  if (st != MLA_OK || empty) return st;
   return from_hip(launch_decode(p, dt == MLA_BF16, stream), "decode launch");
+}
+
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe, const void* latent,
+                                  const void* rope, int64_t lat_bstride, int64_t lat_rstride,
+                                  int64_t rope_bstride, int64_t rope_rstride, int B, int n_h,
+                                  int T, const int32_t* topk_idx, int K, float scale,
+                                  int num_splits, void* out_lat, float* lse, void* workspace,
+                                  size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+  return decode_impl(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride, rope_bstride,
+                     rope_rstride, B, 1, n_h, T, topk_idx, K, 0, scale, num_splits, out_lat, lse,
+                     workspace, ws_bytes, dt, stream);
+}
+
+mla_status mla_decode_latent_attn_multi(const void* q_lat, const void* q_pe, const void* latent,
+                                        const void* rope, int64_t lat_bstride,
+                                        int64_t lat_rstride, int64_t rope_bstride,
+                                        int64_t rope_rstride, int B, int S_q, int n_h, int T,
+                                        const int32_t* topk_idx, int K, int causal, float scale,
+                                        int num_splits, void* out_lat, float* lse,
+                                        void* workspace, size_t ws_bytes, mla_dtype dt,
+                                        hipStream_t stream) {
+  return decode_impl(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride, rope_bstride,
+                     rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale, num_splits,
+                     out_lat, lse, workspace, ws_bytes, dt, stream);
+}
+
+size_t mla_decode_step_workspace_bytes(int B, int S_q, int n_h, int T, int K, int num_splits,
+                                       mla_dtype dt) {
+  if (S_q < 1 || B < 0 || n_h < 1 || static_cast<int64_t>(S_q) * n_h > 65535)
+    return static_cast<size_t>(-1);
+  const size_t attn = mla_decode_workspace_bytes(B, S_q * n_h, T, K, num_splits, dt);
+  if (attn == static_cast<size_t>(-1)) return attn;
+  const size_t esz = dt == MLA_BF16 ? 2 : 4;
+  const size_t lat = align256(static_cast<size_t>(B) * S_q * n_h * D_C * esz);
+  return 2 * lat + attn;
+}
+
+mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv_b,
+                           const void* latent, const void* rope, int64_t lat_bstride,
+                           int64_t lat_rstride, int64_t rope_bstride, int64_t rope_rstride, int B,
+                           int S_q, int n_h, int T, const int32_t* topk_idx, int K, int causal,
+                           float scale, int num_splits, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (S_q < 1 || B < 0 || n_h < 1)
+    return fail(MLA_ERR_INVALID_ARG, "B=%d S_q=%d n_h=%d", B, S_q, n_h);
+  if (static_cast<int64_t>(B) * S_q > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "B * S_q above 2^31 - 1");
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !wkv_b || !out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(out))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  const size_t need = mla_decode_step_workspace_bytes(B, S_q, n_h, T, topk_idx ? K : 0,
+                                                      num_splits, dt);
+  if (need == static_cast<size_t>(-1)) {
+    // let the attention checks name the problem
+    int rows;
+    mla_status st = check_decode_dims(B, n_h, T, K, topk_idx != nullptr, &rows);
+    if (st != MLA_OK) return st;
+    return fail(MLA_ERR_INVALID_ARG, "arguments rejected (S_q * n_h above 65535 or num_splits=%d)",
+                num_splits);
+  }
+  if (!workspace || ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? ws_bytes : static_cast<size_t>(0));
+  if (!aligned16(workspace)) return fail(MLA_ERR_UNSUPPORTED, "misaligned workspace");
+  const size_t esz = dt == MLA_BF16 ? 2 : 4;
+  const size_t lat = align256(static_cast<size_t>(B) * S_q * n_h * D_C * esz);
+  char* ws = static_cast<char*>(workspace);
+  void* q_lat = ws;
+  void* o_lat = ws + lat;
+  const int BS = B * S_q;  // absorb and W^UV see every (sequence, token) as a batch row
+  // every check happens before the first launch
+  DecodeParams p;
+  bool empty;
+  mla_status st = decode_prepare(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride,
+                                 rope_bstride, rope_rstride, B, S_q, n_h, T, topk_idx, K, causal,
+                                 scale, num_splits, o_lat, lse, ws + 2 * lat, ws_bytes - 2 * lat,
+                                 dt, &p, &empty);
+  if (st != MLA_OK) return st;
+  st = from_hip(launch_absorb_q(q_nope, wkv_b, q_lat, BS, n_h, dt == MLA_BF16, stream),
+                "absorb launch");
+  if (st != MLA_OK) return st;
+  st = from_hip(launch_decode(p, dt == MLA_BF16, stream), "decode launch");
+  if (st != MLA_OK) return st;
+  return from_hip(launch_out_up(o_lat, wkv_b, out, BS, n_h, dt == MLA_BF16, stream),
+                  "out_up launch");
 }
 
 mla_status mla_out_up(const void* out_lat, const void* wkv_b, void* out, int B, int n_h,

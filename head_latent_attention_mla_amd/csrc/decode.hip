@@ -216,8 +216,10 @@ __device__ __forceinline__ floatx16 partial_scores(const char* buf, int s_off, c
 
 // FULL: every 128-head group holds 128 real heads (n_h % 128 == 0), which
 // removes the code for head quarters without heads.
-template <bool SPARSE, bool FULL>
+// CAUSAL (dense only): per-head visible row limit of multi-token queries.
+template <bool SPARSE, bool FULL, bool CAUSAL>
 __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
+  static_assert(!(SPARSE && CAUSAL), "the causal limit is for dense attention");
   __shared__ __attribute__((aligned(16))) char tiles[NBUF * BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // partner partial scores
   __shared__ __attribute__((aligned(16))) u32x4 qpe[4 * 4 * 64];  // rotary query operands
@@ -250,6 +252,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const int row_begin = s * p.tiles_per_split * TILE;
   const int row_end = min(p.rows, row_begin + p.tiles_per_split * TILE);
   const int ntiles = (row_end - row_begin + TILE - 1) / TILE;
+  // Rows [row_begin, row_vis) are visible to this lane's head. Heads are
+  // numbered token * n_h_tok + head; with the causal limit, query token j
+  // (position T - s_q + j) sees positions up to its own.
+  const int row_vis = CAUSAL ? min(row_end, p.T - p.s_q + headc / p.n_h_tok + 1) : row_end;
 
   const i32x4 lat_d =
       make_rsrc(static_cast<const uint16_t*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs);
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       // partial scores of tile it+1 (on the last tile they read a stale
       // buffer and are discarded); the partner's multiplies fill the
       // SIMD's MFMA pipe meanwhile ----
-      const int valid = row_end - (row_begin + it * TILE);  // rows of this tile that exist
+      const int valid = row_vis - (row_begin + it * TILE);  // visible rows of this tile
 #pragma unroll
       for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
       float smax = -INFINITY;
@@ -476,10 +482,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       const float tmax = pair_max(smax * sl2);
       const bool rescaled = __any(tmax > m + RESCALE_SLACK);
       const float m_new = rescaled ? fmaxf(m, tmax) : m;
-      const float f = rescaled ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 on the first tile
+      // 0 on the first tile; a head that has seen no visible row yet (causal
+      // limit) keeps m = -inf, factor 1 and weights exp2(-inf) = 0
+      const float f = rescaled && (!CAUSAL || m_new != -INFINITY)
+                          ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
       l *= f;
       m = m_new;
-      const float nm = -m;
+      const float nm = !CAUSAL || m != -INFINITY ? -m : 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 P;
@@ -539,7 +548,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
   if (kh == 1 && active) {
     const float l_tot = pair_sum(l);
-    if (g == 0) linv[hq * 32 + n] = 1.f / l_tot;
+    // a head with no visible row in this split: zero partial, lse -inf
+    if (g == 0) linv[hq * 32 + n] = !CAUSAL || l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (g == 0 && head < p.n_h) {
       const float lse_v = (m + log2f(l_tot)) * LN2;  // natural log of sum exp(z)
       const int64_t bh = static_cast<int64_t>(b) * p.n_h + head;
@@ -682,7 +692,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
   const float* lat = static_cast<const float*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs;
   const float* rp = static_cast<const float*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs;
   const int row_begin = s * p.tiles_per_split * TILE;
-  const int row_end = min(p.rows, row_begin + p.tiles_per_split * TILE);
+  const int row_end_split = min(p.rows, row_begin + p.tiles_per_split * TILE);
+  // head h = token * n_h_tok + head; causal: token j sees up to T - s_q + j
+  const int row_end = (!p.idx && p.causal) ? min(row_end_split, p.T - p.s_q + h / p.n_h_tok + 1)
+                                           : row_end_split;
   __syncthreads();
 
   float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
@@ -707,7 +720,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
     const float tmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     const float m_new = fmaxf(m, tmax);
-    const float f = expf(m - m_new);
+    const float f = m_new != -INFINITY ? expf(m - m_new) : 1.f;
     const float pv = rr < row_end ? expf(t - m_new) : 0.f;
     ps[tid] = pv;
     ts[tid] = tok;
@@ -737,8 +750,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
     dst = static_cast<float*>(p.ws_o) + sbh * D_C;
     lse_dst = p.ws_lse + sbh;
   }
-  dst[tid] = acc0 / l;
-  dst[tid + 256] = acc1 / l;
+  // no visible row in this split (causal limit): zero partial, lse -inf
+  const float linv = l > 0.f ? 1.f / l : 0.f;
+  dst[tid] = acc0 * linv;
+  dst[tid + 256] = acc1 * linv;
   if (tid == 0 && lse_dst) *lse_dst = m + logf(l);
 }
 
@@ -747,8 +762,11 @@ hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream
   if (is_bf16) {
     dim3 grid(p.num_splits, hgroups, p.B);
     const bool full = p.n_h % 128 == 0;
-    auto kern = p.idx ? (full ? decode_bf16_kernel<true, true> : decode_bf16_kernel<true, false>)
-                      : (full ? decode_bf16_kernel<false, true> : decode_bf16_kernel<false, false>);
+    auto kern =
+        p.idx ? (full ? decode_bf16_kernel<true, true, false> : decode_bf16_kernel<true, false, false>)
+        : p.causal
+            ? (full ? decode_bf16_kernel<false, true, true> : decode_bf16_kernel<false, false, true>)
+            : (full ? decode_bf16_kernel<false, true, false> : decode_bf16_kernel<false, false, false>);
     hipLaunchKernelGGL(kern, grid, dim3(NWAVES * 64), 0, stream, p);
   } else {
     hipLaunchKernelGGL(decode_f32_kernel, dim3(p.num_splits, p.n_h, p.B), dim3(256), 0, stream, p);

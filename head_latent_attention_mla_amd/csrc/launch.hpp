@@ -25,7 +25,9 @@ struct DecodeParams {
   const void* latent;
   const void* rope;
   int64_t lat_bs, lat_rs, rope_bs, rope_rs;  // element strides
-  int B, n_h, T;
+  int B, n_h, T;        // n_h counts every query row of a sequence: s_q * n_h_tok
+  int s_q, n_h_tok;     // query tokens per sequence, heads per token
+  int causal;           // token j sees positions < T - s_q + j + 1 (dense only)
   const int32_t* idx;  // nullptr = dense
   int K;
   int rows;            // attended positions per sequence (T or K)

@@ -158,6 +158,62 @@ mla_status mla_decode_latent_attn(const void* q_lat, const void* q_pe,
                                   mla_dtype dt, hipStream_t stream);
 
 /*
+ * Latent attention with S_q query tokens per sequence: the token axis s of
+ * the decode einsums ([ABS] excerpt: q [b,s,h,c] against the cache [b,t,c],
+ * scores [b,s,h,t]). T counts the cached positions including the S_q new
+ * tokens, which sit at positions T-S_q .. T-1 (append them first, e.g. with
+ * mla_cache_append). For sequence b, token j < S_q, head h < n_h:
+ *   z[b,j,h,t] = scale * (q_lat[b,j,h,:] . latent[b,t,:] + q_pe[b,j,h,:] . rope[b,t,:])
+ * over t < T, with
+ *   - topk_idx (int32 [B, K] or NULL): one index set per sequence shared by
+ *     all tokens and heads ([ABS] excerpt: the mask has a singleton token
+ *     axis); same contract as mla_decode_latent_attn;
+ *   - causal != 0: token j sees only t <= T - S_q + j (the causal mask of
+ *     the [VUP] prefill excerpt, for queries at the end of the cache);
+ *     requires T >= S_q and dense attention (topk_idx NULL; otherwise
+ *     MLA_ERR_UNSUPPORTED).
+ *   p = softmax_t z, out_lat[b,j,h,:] = sum_t p * latent[b,t,:],
+ *   lse[b,j,h] = log sum_t exp z (optional).
+ * q_lat [B, S_q, n_h, 512], q_pe [B, S_q, n_h, 64], out_lat [B, S_q, n_h, 512]
+ * (dt), lse [B, S_q, n_h] float32. Cache arguments, num_splits and the
+ * workspace are those of mla_decode_latent_attn for n_h' = S_q * n_h query
+ * rows: size the workspace with mla_decode_workspace_bytes(B, S_q * n_h, T,
+ * K, num_splits, dt). S_q * n_h <= 65535. S_q == 1 with causal == 0 is
+ * mla_decode_latent_attn. The S_q tokens of a sequence share one read of
+ * each cache tile when S_q * n_h <= 128 (e.g. a tensor-parallel share of
+ * the heads).
+ */
+mla_status mla_decode_latent_attn_multi(const void* q_lat, const void* q_pe, const void* latent,
+                                        const void* rope, int64_t lat_bstride,
+                                        int64_t lat_rstride, int64_t rope_bstride,
+                                        int64_t rope_rstride, int B, int S_q, int n_h, int T,
+                                        const int32_t* topk_idx, int K, int causal, float scale,
+                                        int num_splits, void* out_lat, float* lse,
+                                        void* workspace, size_t ws_bytes, mla_dtype dt,
+                                        hipStream_t stream);
+
+/*
+ * The whole absorbed decode step in one call ([ABS] excerpt: absorb W^UK,
+ * latent attention, W^UV): enqueues mla_absorb_q on B*S_q rows,
+ * mla_decode_latent_attn_multi and mla_out_up on B*S_q rows, with q_lat and
+ * out_lat kept in the workspace.
+ *   q_nope [B, S_q, n_h, 128], q_pe [B, S_q, n_h, 64], wkv_b [n_h*256, 512],
+ *   out [B, S_q, n_h, 128] (dt), lse [B, S_q, n_h] float32 or NULL; cache,
+ *   topk_idx, causal, scale and num_splits as in mla_decode_latent_attn_multi.
+ *   workspace: at least mla_decode_step_workspace_bytes(B, S_q, n_h, T, K,
+ *   num_splits, dt) bytes ((size_t)-1 for arguments the call would reject).
+ * Every argument is checked before the first kernel is enqueued.
+ */
+size_t mla_decode_step_workspace_bytes(int B, int S_q, int n_h, int T, int K, int num_splits,
+                                       mla_dtype dt);
+mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv_b,
+                           const void* latent, const void* rope, int64_t lat_bstride,
+                           int64_t lat_rstride, int64_t rope_bstride, int64_t rope_rstride, int B,
+                           int S_q, int n_h, int T, const int32_t* topk_idx, int K, int causal,
+                           float scale, int num_splits, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, mla_dtype dt, hipStream_t stream);
+
+/*
  * W^UV after the probability-weighted sum ([KVR] "How it works", second
  * absorb identity, and "Watch-outs": attend on the latent, then W^UV;
  * [ABS] excerpt, last einsum; [VUP] "Explanation": value rows are 128..255

@@ -117,6 +117,45 @@ def test_reconstruct_argument_errors(lib):
     assert lib.mla_kv_reconstruct(None, None, None, None, None, 0, 16, BF16, s) == OK
 
 
+def multi(lib, **kw):
+    a = dict(q_lat=FAKE, q_pe=FAKE, latent=FAKE, rope=FAKE, lbs=4096 * 576, lrs=576,
+             rbs=4096 * 576, rrs=576, B=2, S=2, n_h=128, T=4096, idx=None, K=0, causal=1,
+             scale=0.07, splits=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, dt=BF16,
+             stream=None)
+    a.update(kw)
+    return lib.mla_decode_latent_attn_multi(
+        a["q_lat"], a["q_pe"], a["latent"], a["rope"], a["lbs"], a["lrs"], a["rbs"], a["rrs"],
+        a["B"], a["S"], a["n_h"], a["T"], a["idx"], a["K"], a["causal"], a["scale"], a["splits"],
+        a["out"], a["lse"], a["ws"], a["ws_bytes"], a["dt"], a["stream"])
+
+
+def test_multi_token_argument_errors(lib):
+    assert multi(lib, S=0) == INVALID
+    assert multi(lib, T=3, S=4) == INVALID                    # causal needs T >= S_q
+    assert multi(lib, idx=FAKE, K=64) == UNSUPPORTED           # causal + index set
+    assert multi(lib, S=600) == UNSUPPORTED                    # S_q * n_h above 65535
+    assert multi(lib, q_lat=None) == INVALID
+    assert multi(lib, ws=None) == WORKSPACE
+    assert multi(lib, B=0, q_lat=None) == OK
+    # the step: argument errors before anything is enqueued
+    step = lib.mla_decode_step
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4096 * 576, 576, 4096 * 576, 576, 2, 2, 128, 4096,
+            None, 0, 1, 0.07, 0, FAKE, None, FAKE, 1 << 30, BF16, None]
+    bad = list(args); bad[0] = None
+    assert step(*bad) == INVALID
+    bad = list(args); bad[20] = None
+    assert step(*bad) == WORKSPACE
+    bad = list(args); bad[21] = 100
+    assert step(*bad) == WORKSPACE
+    bad = list(args); bad[12] = 1                              # T=1 < S_q=2, causal
+    assert step(*bad) == INVALID
+    bad = list(args); bad[16] = float("nan")
+    assert step(*bad) == INVALID
+    need = binding.mla_decode_step_workspace_bytes(2, 2, 128, 4096)
+    # q_lat and out_lat (2*2*128*512 bf16 each) plus the split partials
+    assert need >= 2 * (2 * 2 * 128 * 512 * 2) + binding.mla_decode_workspace_bytes(2, 256, 4096)
+
+
 def append(lib, **kw):
     a = dict(kv=FAKE, rs=576, gamma=FAKE, eps=1e-6, freqs=FAKE, n_pos=4096, seq=None, pos=FAKE,
              N=8, lat=FAKE, rope=FAKE, lbs=4096 * 576, lrs=576, rbs=4096 * 576, rrs=576,

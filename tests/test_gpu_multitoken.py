@@ -1,0 +1,154 @@
+"""GPU parity of multi-token decode (S_q query tokens per sequence, optional
+causal limit at the end of the cache, shared index set) and of the one-call
+decode step, against the fp64 oracle.
+
+Bar: max|err| <= 2e-2 * max|ref| for bf16, 1e-5 * max|ref| for fp32, for
+out_lat / out and for the log-sum-exp. Cases cover full and partial 128-row
+head groups, splits whose rows are all hidden from some tokens by the causal
+limit, a query block that fills the whole cache (T == S_q), and the decode
+workload's sizes (sampled sequences).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_latent_attention_mla_amd import binding as mla
+from head_latent_attention_mla_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check(got, ref, tol, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    m = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    assert err <= tol * m, f"{what}: max|err| {err:.3e} > {tol} * {m:.3e}"
+
+
+def multi_inputs(B, S_q, n_h, T, dtype, seed, topk=None):
+    """Query rows [B, S_q, n_h, .] and a cache from the shared generators: the
+    S_q tokens of sequence b are drawn as B*S_q single-token rows."""
+    base = synth.decode_inputs(B * S_q, n_h, 1, dtype, seed=seed, stage_inputs=True)
+    cache = synth.decode_inputs(B, 1, T, dtype, seed=seed + 1, topk=topk)
+    out = {
+        "q_lat": base["q_lat"].reshape(B, S_q, n_h, 512).contiguous(),
+        "q_pe": base["q_pe"].reshape(B, S_q, n_h, 64).contiguous(),
+        "q_nope": base["q_nope"].reshape(B, S_q, n_h, 128).contiguous(),
+        "wkv_b": base["wkv_b"],
+        "cache": cache["cache"],
+    }
+    if topk:
+        out["topk_idx"] = cache["topk_idx"]
+    return out
+
+
+MULTI_CASES = [
+    # B, S_q, n_h, T, dtype, causal, topk, num_splits
+    (2, 2, 128, 700, torch.bfloat16, True, None, 0),     # two full head groups
+    (3, 4, 16, 333, torch.bfloat16, True, None, 0),      # 64 rows: one partial group
+    (2, 3, 16, 100, torch.bfloat16, False, None, 0),
+    (2, 4, 16, 33, torch.bfloat16, True, None, 2),       # split 1 = row 32, hidden from 3 tokens
+    (1, 5, 16, 5, torch.bfloat16, True, None, 0),        # T == S_q: token 0 sees one row
+    (2, 2, 128, 1000, torch.bfloat16, False, 300, 0),    # shared index set
+    (2, 3, 16, 65, torch.float32, True, None, 0),
+    (2, 4, 16, 33, torch.float32, True, None, 2),
+]
+
+
+@pytest.mark.parametrize("B,S_q,n_h,T,dtype,causal,topk,splits", MULTI_CASES)
+def test_multi_token_latent_attention(B, S_q, n_h, T, dtype, causal, topk, splits):
+    inp = multi_inputs(B, S_q, n_h, T, dtype, seed=B * 1000 + S_q * 100 + T, topk=topk)
+    cache = inp["cache"].to(DEV)
+    idx = inp.get("topk_idx")
+    out, lse = mla.mla_decode_latent_attn_multi(
+        inp["q_lat"].to(DEV), inp["q_pe"].to(DEV), cache[..., :512], cache[..., 512:],
+        topk_idx=None if idx is None else idx.to(DEV), causal=causal, num_splits=splits,
+        want_lse=True)
+    ref, ref_lse = oracle.latent_attention_multi(inp["q_lat"], inp["q_pe"],
+                                                 inp["cache"][..., :512], inp["cache"][..., 512:],
+                                                 topk_idx=idx, causal=causal)
+    check(f64(out), ref, TOL[dtype], "out_lat")
+    check(f64(lse), ref_lse, TOL[dtype], "lse")
+
+
+def test_multi_token_with_one_token_matches_single_token_call():
+    inp = multi_inputs(4, 1, 128, 300, torch.bfloat16, seed=7)
+    cache = inp["cache"].to(DEV)
+    a = mla.mla_decode_latent_attn_multi(inp["q_lat"].to(DEV), inp["q_pe"].to(DEV),
+                                         cache[..., :512], cache[..., 512:])
+    b = mla.mla_decode_latent_attn(inp["q_lat"][:, 0].contiguous().to(DEV),
+                                   inp["q_pe"][:, 0].contiguous().to(DEV), cache[..., :512],
+                                   cache[..., 512:])
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, 0].cpu().view(torch.int16), b.cpu().view(torch.int16))
+
+
+def oracle_step(inp, causal, idx=None, sel=None):
+    """absorb -> multi-token latent attention -> W^UV, all in double."""
+    qn, qp, cache = inp["q_nope"], inp["q_pe"], inp["cache"]
+    if sel is not None:
+        qn, qp, cache = qn[sel], qp[sel], cache[sel]
+        idx = None if idx is None else idx[sel]
+    B, S_q, n_h, _ = qn.shape
+    w = inp["wkv_b"]
+    q_lat = oracle.absorb_q(qn.reshape(B * S_q, n_h, 128), w).reshape(B, S_q, n_h, 512)
+    o, lse = oracle.latent_attention_multi(q_lat, qp, cache[..., :512], cache[..., 512:],
+                                           topk_idx=idx, causal=causal)
+    out = oracle.out_up(o.reshape(B * S_q, n_h, 512), w).reshape(B, S_q, n_h, 128)
+    return out, lse
+
+
+@pytest.mark.parametrize("B,S_q,n_h,T,dtype,causal,topk", [
+    (2, 2, 128, 517, torch.bfloat16, True, None),
+    (3, 1, 128, 300, torch.bfloat16, False, 100),
+    (2, 4, 16, 90, torch.bfloat16, True, None),
+    (2, 2, 16, 70, torch.float32, True, None),
+])
+def test_decode_step_one_call(B, S_q, n_h, T, dtype, causal, topk):
+    inp = multi_inputs(B, S_q, n_h, T, dtype, seed=31 + T, topk=topk)
+    cache = inp["cache"].to(DEV)
+    idx = inp.get("topk_idx")
+    out, lse = mla.mla_decode_step(inp["q_nope"].to(DEV), inp["q_pe"].to(DEV),
+                                   inp["wkv_b"].to(DEV), cache[..., :512], cache[..., 512:],
+                                   topk_idx=None if idx is None else idx.to(DEV), causal=causal,
+                                   want_lse=True)
+    ref, ref_lse = oracle_step(inp, causal, idx)
+    check(f64(out), ref, TOL[dtype], "out")
+    check(f64(lse), ref_lse, TOL[dtype], "lse")
+
+
+def test_decode_step_single_token_equals_the_three_calls():
+    inp = synth.config_inputs(2)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    cache = d["cache"]
+    one = mla.mla_decode_step(d["q_nope"], d["q_pe"], d["wkv_b"], cache[..., :512],
+                              cache[..., 512:])
+    q_lat = mla.mla_absorb_q(d["q_nope"], d["wkv_b"])
+    o_lat = mla.mla_decode_latent_attn(q_lat, d["q_pe"], cache[..., :512], cache[..., 512:])
+    three = mla.mla_out_up(o_lat, d["wkv_b"])
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu().view(torch.int16), three.cpu().view(torch.int16))
+
+
+def test_decode_step_causal_pair_at_decode_workload_size_sampled():
+    # B=32 sequences of T=4096 cached positions, n_h=128, two query tokens
+    # per sequence (the second one sees one more position); three sequences
+    # are checked against the oracle
+    B, S_q, n_h, T = 32, 2, 128, 4096
+    inp = multi_inputs(B, S_q, n_h, T, torch.bfloat16, seed=1002)
+    cache = inp["cache"].to(DEV)
+    out = mla.mla_decode_step(inp["q_nope"].to(DEV), inp["q_pe"].to(DEV), inp["wkv_b"].to(DEV),
+                              cache[..., :512], cache[..., 512:], causal=True)
+    sel = [0, 17, 31]
+    ref, _ = oracle_step(inp, True, sel=sel)
+    check(f64(out.cpu()[sel]), ref, TOL[torch.bfloat16], "out")
