@@ -20,6 +20,8 @@ Parity status (all pinned by ``tests/test_oracle_*.py``):
   kv_reconstruct      pinned: structured weights with a closed form
   latent_attention_multi  pinned: s_q = 1 case, per-token reduction to
                       latent_attention (causal prefix / full), hand corner
+  attention_naive     pinned: torch SDPA (double) with the same mask, first
+                      causal row, one-query reduction to decode_naive
   cache_append        pinned: RMSNorm closed forms (constant, scaled, unit
                       RMS), rotation by quarter turns, composition, pairing
 """
@@ -69,11 +71,12 @@ def _load():
         lib.orc_softmax_scale.restype = D
         lib.orc_latent_attention_multi.argtypes = [P, I, P, I, P, P, I, L, L, L, L, I, I, I,
                                                    I, I, I, P, I, I, D, P, P]
+        lib.orc_attention_naive.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, D, P, P]
         lib.orc_cache_append.argtypes = [P, P, I, P, P, P, L, L, I, I, D, P, P]
         for name in ("orc_dequant_fp8_block", "orc_absorb_q", "orc_latent_attention",
                      "orc_out_up", "orc_decode_absorbed", "orc_kv_reconstruct",
                      "orc_decode_naive", "orc_cache_append",
-                     "orc_latent_attention_multi"):
+                     "orc_latent_attention_multi", "orc_attention_naive"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -316,3 +319,30 @@ def cache_append(kv, k_pe, gamma, freqs, pos, eps=1e-6):
                                     f.shape[0], d_c, d_r, float(eps), _ptr(lat), _ptr(rope)),
            "cache_append")
     return lat, rope
+
+
+def attention_naive(q, k, v, topk_idx=None, causal=False, scale=192 ** -0.5):
+    """Ordinary attention over reconstructed keys and values: q [B,S,n_h,d_qk],
+    k [B,T,n_h,d_qk], v [B,T,n_h,d_v]; topk_idx int32 [B,S,K] (one index set
+    per query token) or None; causal: query s sees t <= T - S + s.
+    Returns (out [B,S,n_h,d_v], lse [B,S,n_h]) in double."""
+    qq = np.ascontiguousarray(_np(q))
+    kk = np.ascontiguousarray(_np(k))
+    vv = np.ascontiguousarray(_np(v))
+    assert qq.dtype == kk.dtype == vv.dtype
+    B, S, n_h, d_qk = qq.shape
+    T = kk.shape[1]
+    assert kk.shape == (B, T, n_h, d_qk) and vv.shape[:3] == (B, T, n_h)
+    d_v = vv.shape[3]
+    K = 0
+    idx = None
+    if topk_idx is not None:
+        idx = np.ascontiguousarray(_np(topk_idx), dtype=np.int32)
+        assert idx.shape[:2] == (B, S)
+        K = idx.shape[2]
+    out = np.empty((B, S, n_h, d_v), np.float64)
+    lse = np.empty((B, S, n_h), np.float64)
+    _check(_load().orc_attention_naive(_ptr(qq), _ptr(kk), _ptr(vv), _dt(qq), B, S, T, n_h,
+                                       d_qk, d_v, _ptr(idx), K, int(causal), float(scale),
+                                       _ptr(out), _ptr(lse)), "attention_naive")
+    return out, lse

@@ -562,3 +562,77 @@ int orc_cache_append(const void* kv, const void* k_pe, int dt_in, const float* g
   }
   return 0;
 }
+
+/* ---- ordinary attention over reconstructed keys and values ---------------
+ * "Value up-projection", prefill excerpt: q = [q_nope ; q_pe] per head,
+ * scores = q . k for every (query s, key t) times the scale, plus the index
+ * mask (per query token: -inf outside that token's index set, scattered from
+ * its own row of indices) and the causal mask, softmax over t, then the
+ * probability-weighted sum of the values. Queries sit at the end of the key
+ * sequence: query s is position T - S + s (T == S in the excerpt, where the
+ * causal mask lets s see t <= s).
+ *   q   [B, S, n_h, d_qk],  k [B, T, n_h, d_qk],  v [B, T, n_h, d_v]
+ *   idx int32 [B, S, K] or NULL;  causal: t <= T - S + s
+ *   out [B, S, n_h, d_v] (double), lse [B, S, n_h] (optional)
+ * A query with no visible key gets a zero output and lse = -inf.
+ * Parity: pinned (torch scaled_dot_product_attention in double with the
+ * same boolean mask; hand-checked first causal row; reduction of one query
+ * to the naive decode path). */
+int orc_attention_naive(const void* q, const void* k, const void* v, int dt, int B, int S,
+                        int T, int n_h, int d_qk, int d_v, const int32_t* idx, int K,
+                        int causal, double scale, double* out, double* lse) {
+  if (B < 0 || S < 0 || T < 1 || n_h < 1 || d_qk < 1 || d_v < 1) return -1;
+  if (idx && (K < 1 || K > T)) return -1;
+  if (causal && T < S) return -1;
+  int bad = 0;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+  for (int b = 0; b < B; b++)
+    for (int s = 0; s < S; s++)
+      for (int h = 0; h < n_h; h++) {
+        unsigned char* al = (unsigned char*)malloc((size_t)T);
+        double* z = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!al || !z ||
+            build_allowed(idx ? idx + ((int64_t)b * S + s) * K : NULL, K, T, al)) {
+#pragma omp atomic write
+          bad = 1;
+          free(al);
+          free(z);
+          continue;
+        }
+        int any = 0;
+        for (int t = 0; t < T; t++) {
+          if (causal && t > T - S + s) al[t] = 0;
+          any |= al[t];
+        }
+        const int64_t row = ((int64_t)b * S + s) * n_h + h;
+        if (!any) {
+          for (int d = 0; d < d_v; d++) out[row * d_v + d] = 0.0;
+          if (lse) lse[row] = -INFINITY;
+          free(al);
+          free(z);
+          continue;
+        }
+        for (int t = 0; t < T; t++) {
+          if (!al[t]) {
+            z[t] = -INFINITY;
+            continue;
+          }
+          const int64_t krow = ((int64_t)b * T + t) * n_h + h;
+          double acc = 0.0;
+          for (int e = 0; e < d_qk; e++)
+            acc += load(q, row * d_qk + e, dt) * load(k, krow * d_qk + e, dt);
+          z[t] = scale * acc;
+        }
+        double l = softmax_inplace(z, al, T);
+        if (lse) lse[row] = l;
+        for (int d = 0; d < d_v; d++) {
+          double acc = 0.0;
+          for (int t = 0; t < T; t++)
+            if (al[t]) acc += z[t] * load(v, (((int64_t)b * T + t) * n_h + h) * d_v + d, dt);
+          out[row * d_v + d] = acc;
+        }
+        free(al);
+        free(z);
+      }
+  return bad ? -1 : 0;
+}

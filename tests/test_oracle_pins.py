@@ -614,3 +614,77 @@ def test_causal_with_an_index_set_that_hides_every_visible_row():
     assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(lse[0, 0]))
     np.testing.assert_allclose(o[0, 2], np.broadcast_to(p["latent"][0, T - 1], (n_h, 16)),
                                rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# ordinary attention over reconstructed keys and values (prefill excerpt)
+# --------------------------------------------------------------------------
+
+def _naive_problem(seed, B, S, T, n_h, d_qk=12, d_v=5):
+    g = rng(seed)
+    return (g.standard_normal((B, S, n_h, d_qk)), g.standard_normal((B, T, n_h, d_qk)),
+            g.standard_normal((B, T, n_h, d_v)))
+
+
+@pytest.mark.parametrize("S,T,causal,K", [(7, 7, True, None), (5, 11, True, 4),
+                                          (6, 9, False, 3), (4, 4, False, None)])
+def test_attention_naive_matches_torch_sdpa(S, T, causal, K):
+    B, n_h = 2, 3
+    q, k, v = _naive_problem(61 + S + T, B, S, T, n_h)
+    allowed = np.ones((B, S, T), bool)
+    idx = None
+    if K:
+        g = rng(62)
+        # every query keeps at least one visible key: the last row of the set
+        # is its own position
+        idx = np.empty((B, S, K), np.int32)
+        for b in range(B):
+            for s in range(S):
+                own = T - S + s
+                others = g.choice(np.delete(np.arange(T), own), K - 1, replace=False)
+                idx[b, s] = np.concatenate([others, [own]])
+        allowed[:] = False
+        for b in range(B):
+            for s in range(S):
+                allowed[b, s, idx[b, s]] = True
+    if causal:
+        allowed &= np.arange(T)[None, None, :] <= (T - S + np.arange(S))[None, :, None]
+    out, lse = oracle.attention_naive(q, k, v, topk_idx=idx, causal=causal, scale=0.35)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    mask = torch.from_numpy(allowed)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                           scale=0.35)
+    np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-12)
+    z = 0.35 * torch.einsum("bhsd,bhtd->bhst", tq, tk).masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(z, -1).permute(0, 2, 1).numpy(), rtol=1e-12)
+
+
+def test_attention_naive_first_causal_row_and_hidden_queries():
+    B, S, T, n_h = 1, 4, 4, 2
+    q, k, v = _naive_problem(63, B, S, T, n_h)
+    out, lse = oracle.attention_naive(q, k, v, causal=True, scale=0.5)
+    np.testing.assert_allclose(out[0, 0], v[0, 0], rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], 0.5 * np.sum(q[0, 0] * k[0, 0], -1), rtol=1e-13)
+    # an index set that lies wholly after a query hides every key from it
+    idx = np.full((B, S, 1), T - 1, np.int32)
+    out, lse = oracle.attention_naive(q, k, v, topk_idx=idx, causal=True)
+    assert np.all(out[0, :3] == 0.0) and np.all(np.isneginf(lse[0, :3]))
+    np.testing.assert_allclose(out[0, 3], v[0, 3], rtol=1e-14)
+
+
+def test_attention_naive_one_query_equals_the_naive_decode():
+    # reconstruct K and V with the reconstruction function, attend with one
+    # query at the end: the naive decode does both steps itself
+    p = tiny_problem(65, 2, 3, 9)
+    idx = np.stack([rng(66 + b).choice(9, 4, replace=False) for b in range(2)]).astype(np.int32)
+    ref = oracle.decode_naive(p["q_nope"], p["q_pe"], p["latent"], p["rope"], p["w"],
+                              topk_idx=idx, scale=0.3, d_n=p["d_n"], d_v=p["d_v"])["out"]
+    B, T = 2, 9
+    K, V = oracle.kv_reconstruct(p["latent"].reshape(B * T, -1), p["rope"].reshape(B * T, -1),
+                                 p["w"], 3, d_n=p["d_n"], d_v=p["d_v"])
+    q = np.concatenate([p["q_nope"], p["q_pe"]], -1)[:, None]
+    out, _ = oracle.attention_naive(q, K.reshape(B, T, 3, -1), V.reshape(B, T, 3, -1),
+                                    topk_idx=idx[:, None], causal=True, scale=0.3)
+    np.testing.assert_allclose(out[:, 0], ref, rtol=1e-12, atol=1e-13)
