@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["dequant.hip", "absorb.hip", "out_up.hip", "decode.hip", "reconstruct.hip", "append.hip",
+SOURCES = ["dequant.hip", "absorb.hip", "out_up.hip", "decode.hip", "reconstruct.hip", "append.hip", "attention.hip",
            "capi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -64,11 +64,15 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_step_workspace_bytes.restype = Z
         lib.mla_decode_step.argtypes = [P, P, P, P, P, L, L, L, L, I, I, I, I, P, I, I, F, I, P,
                                         P, P, Z, I, P]
+        lib.mla_attention_naive_workspace_bytes.argtypes = [I, I, I, I]
+        lib.mla_attention_naive_workspace_bytes.restype = Z
+        lib.mla_attention_naive.argtypes = [P, P, P, I, I, I, I, P, I, I, F, P, P, P, Z, I, P]
         lib.mla_cache_append.argtypes = [P, L, P, F, P, I, P, P, L, P, P, L, L, L, L, I, I, I,
                                          P]
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
                      "mla_out_up", "mla_kv_reconstruct", "mla_cache_append",
-                     "mla_decode_latent_attn_multi", "mla_decode_step"):
+                     "mla_decode_latent_attn_multi", "mla_decode_step",
+                     "mla_attention_naive"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -416,3 +420,54 @@ def mla_cache_append(kv_a: torch.Tensor, gamma: torch.Tensor, freqs: torch.Tenso
         _ptr(seq_idx), _ptr(pos), N, _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B_cache,
         T_cache, _dtype_code(kv_a), _stream(stream)))
     return latent, rope
+
+
+def mla_attention_naive_workspace_bytes(B: int, S: int, T: int, K: int = 0) -> int:
+    v = library().mla_attention_naive_workspace_bytes(B, S, T, K)
+    if v == ctypes.c_size_t(-1).value:
+        raise MLAError("mla_attention_naive_workspace_bytes", 1, "arguments rejected")
+    return v
+
+
+def mla_attention_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        topk_idx: torch.Tensor = None, causal: bool = False,
+                        scale: float = SCALE, out: torch.Tensor = None, lse: torch.Tensor = None,
+                        workspace: torch.Tensor = None, want_lse: bool = False, stream=None):
+    """Ordinary attention over reconstructed keys and values: q [B, S, n_h,
+    192], k [B, T, n_h, 192], v [B, T, n_h, 128] (k, v as written by
+    mla_kv_reconstruct for N = B*T tokens, viewed per sequence); topk_idx
+    int32 [B, S, K] (one index set per query) or None; causal: query s sees
+    keys up to T - S + s. Returns out [B, S, n_h, 128] (and lse [B, S, n_h])."""
+    _dev(q, k, v, topk_idx, out, lse, workspace)
+    _require(q.dim() == 4 and q.shape[3] == 192 and q.is_contiguous(),
+             "q must be contiguous [B, S, n_h, 192]")
+    B, S, n_h, _ = q.shape
+    _require(k.dtype == q.dtype and k.is_contiguous() and k.dim() == 4 and k.shape[0] == B and
+             k.shape[2] == n_h and k.shape[3] == 192, "k must be contiguous [B, T, n_h, 192]")
+    T = k.shape[1]
+    _require(v.dtype == q.dtype and v.is_contiguous() and tuple(v.shape) == (B, T, n_h, 128),
+             "v must be contiguous [B, T, n_h, 128]")
+    K = 0
+    if topk_idx is not None:
+        _require(topk_idx.dtype == torch.int32 and topk_idx.is_contiguous() and
+                 topk_idx.dim() == 3 and tuple(topk_idx.shape[:2]) == (B, S),
+                 "topk_idx must be contiguous int32 [B, S, K]")
+        K = topk_idx.shape[2]
+    if out is None:
+        out = torch.empty((B, S, n_h, 128), dtype=q.dtype, device=q.device)
+    _require(out.dtype == q.dtype and out.is_contiguous() and tuple(out.shape) == (B, S, n_h, 128),
+             "out must be contiguous [B, S, n_h, 128]")
+    if lse is None and want_lse:
+        lse = torch.empty((B, S, n_h), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and
+                 tuple(lse.shape) == (B, S, n_h), "lse must be contiguous float32 [B, S, n_h]")
+    need = mla_attention_naive_workspace_bytes(B, S, T, K) if B > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_attention_naive", library().mla_attention_naive(
+        _ptr(q), _ptr(k), _ptr(v), B, S, T, n_h, _ptr(topk_idx), K, int(bool(causal)),
+        float(scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _dtype_code(q),
+        _stream(stream)))
+    return (out, lse) if (want_lse or lse is not None) else out

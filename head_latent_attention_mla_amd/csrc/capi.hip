@@ -386,6 +386,66 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope, const void* wkv
                   "kv_reconstruct launch");
 }
 
+size_t mla_attention_naive_workspace_bytes(int B, int S, int T, int K) {
+  if (B < 0 || S < 0 || T < 1 || K < 0 || K > T) return static_cast<size_t>(-1);
+  if (K == 0) return 0;
+  const int64_t qb = attention_query_block(), kt = attention_key_tile();
+  const int64_t words = (T + kt - 1) / kt * (kt / 32);
+  const int64_t s_pad = (S + qb - 1) / qb * qb;
+  return static_cast<size_t>(B) * static_cast<size_t>(words) * static_cast<size_t>(s_pad) * 4;
+}
+
+mla_status mla_attention_naive(const void* q, const void* k, const void* v, int B, int S, int T,
+                               int n_h, const int32_t* topk_idx, int K, int causal, float scale,
+                               void* out, float* lse, void* workspace, size_t ws_bytes,
+                               mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 0 || S < 0 || T < 1 || n_h < 1)
+    return fail(MLA_ERR_INVALID_ARG, "B=%d S=%d T=%d n_h=%d", B, S, T, n_h);
+  if (topk_idx && (K < 1 || K > T))
+    return fail(MLA_ERR_INVALID_ARG, "index count K=%d outside [1, T=%d]", K, T);
+  if (causal && T < S) return fail(MLA_ERR_INVALID_ARG, "causal with T=%d < S=%d", T, S);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (B == 0 || S == 0) return MLA_OK;
+  if (!q || !k || !v || !out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3)))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  if (n_h > 65535 || B > 65535 || (dt == MLA_F32 && S > INT32_MAX))
+    return fail(MLA_ERR_UNSUPPORTED, "B or n_h above 65535");
+  const int qb = attention_query_block();
+  const int64_t nqb = (static_cast<int64_t>(S) + qb - 1) / qb;
+  if (nqb * n_h * B > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 workgroups");
+  // key rows are fetched with 32-bit byte offsets within a 64-key tile
+  if (static_cast<int64_t>(n_h) * 192 * (dt == MLA_BF16 ? 2 : 4) * 64 > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "n_h too large");
+  const size_t need = mla_attention_naive_workspace_bytes(B, S, T, topk_idx ? K : 0);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? ws_bytes : static_cast<size_t>(0));
+  if (need > 0 && !aligned16(workspace)) return fail(MLA_ERR_UNSUPPORTED, "misaligned workspace");
+  AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.mask = static_cast<uint32_t*>(workspace);
+  p.B = B;
+  p.S = S;
+  p.T = T;
+  p.n_h = n_h;
+  p.nqb = static_cast<int>(nqb);
+  const int kt = attention_key_tile();
+  p.mask_words = (T + kt - 1) / kt * (kt / 32);
+  p.s_pad = static_cast<int>(nqb * qb);
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  return from_hip(launch_attention(p, topk_idx, topk_idx ? K : 0, dt == MLA_BF16, stream),
+                  "attention launch");
+}
+
 mla_status mla_cache_append(const void* kv_a, int64_t in_rstride, const float* gamma, float eps,
                             const float* freqs, int n_pos, const int32_t* seq_idx,
                             const int32_t* pos, int64_t N, void* latent, void* rope,

@@ -60,4 +60,25 @@ struct AppendParams {
 
 hipError_t launch_cache_append(const AppendParams& p, bool is_bf16, hipStream_t stream);
 
+struct AttnParams {
+  const void* q;     // [B, S, n_h, 192]
+  const void* k;     // [B, T, n_h, 192]
+  const void* v;     // [B, T, n_h, 128]
+  void* out;         // [B, S, n_h, 128]
+  float* lse;        // [B, S, n_h] or nullptr
+  uint32_t* mask;    // [B, mask_words, s_pad] bits (index sets) or nullptr
+  int B, S, T, n_h;
+  int nqb;           // query blocks per (sequence, head)
+  int mask_words;    // key words per sequence (a multiple of 2)
+  int s_pad;         // nqb * query block
+  float scale;
+  int causal;
+};
+
+// queries per workgroup and keys per tile of the bf16 attention kernel
+int attention_query_block();
+int attention_key_tile();
+hipError_t launch_attention(AttnParams p, const int32_t* idx, int K, bool is_bf16,
+                            hipStream_t stream);
+
 }  // namespace mla

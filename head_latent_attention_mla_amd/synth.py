@@ -28,6 +28,13 @@ kv_a, gain, angles, positions):
            float32 (cos, sin) pairs
   pos      per row: the sequence's current length, ~ U[0, T) (decode), or
            consecutive positions (prefill)
+  q, k, v  per-head queries [B,S,n_h,192], keys [B,T,n_h,192] and values
+           [B,T,n_h,128] of the naive path ~ N(0,1) (the spread of the
+           reconstructed k_nope / v for the weights above, and of k^R)
+  sets     per query token, K distinct key positions: drawn uniformly from
+           the keys the query may see (t <= T - S + s under the causal mask)
+           and, when fewer than K are visible, topped up with hidden ones (as
+           a top-k over masked scores would)
 Values are rounded once to the storage type (bf16 round-to-nearest-even via
 torch, or kept float32).
 """
@@ -40,7 +47,7 @@ D_C, D_R, D_N, D_V = 512, 64, 128, 128
 SCALE = 192 ** -0.5
 
 _ORDER = ("latent", "rope", "q_nope", "q_pe", "wkv_b", "scales", "topk", "q_lat", "o_lat",
-          "kv_a", "gain", "angles", "pos")
+          "kv_a", "gain", "angles", "pos", "q", "k", "v", "sets")
 
 
 def _streams(seed: int) -> dict:
@@ -146,6 +153,30 @@ def append_inputs(N: int, B: int, T: int, dtype=torch.bfloat16, seed: int = 0,
     else:
         assert N <= B
         out["pos"] = torch.from_numpy(g["pos"].integers(0, T, size=N).astype(np.int32))
+    return out
+
+
+def attention_inputs(B: int, S: int, T: int, n_h: int, dtype=torch.bfloat16, seed: int = 0,
+                     topk: int | None = None, causal: bool = True) -> dict:
+    """q [B,S,n_h,192], k [B,T,n_h,192], v [B,T,n_h,128] and, with topk,
+    topk_idx int32 [B,S,topk] (one set per query token)."""
+    g = _streams(seed)
+    out = {
+        "q": _store(_normal(g["q"], (B, S, n_h, D_N + D_R)), dtype),
+        "k": _store(_normal(g["k"], (B, T, n_h, D_N + D_R)), dtype),
+        "v": _store(_normal(g["v"], (B, T, n_h, D_V)), dtype),
+    }
+    if topk is not None:
+        assert 1 <= topk <= T
+        idx = np.empty((B, S, topk), np.int32)
+        for b in range(B):
+            # random priorities; visible keys first, then hidden ones
+            pri = g["sets"].random((S, T), dtype=np.float32)
+            if causal:
+                hidden = np.arange(T)[None, :] > (T - S + np.arange(S))[:, None]
+                pri = pri + hidden.astype(np.float32) * 2.0
+            idx[b] = np.argpartition(pri, topk - 1, axis=1)[:, :topk]
+        out["topk_idx"] = torch.from_numpy(idx)
     return out
 
 

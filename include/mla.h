@@ -240,6 +240,34 @@ mla_status mla_kv_reconstruct(const void* c, const void* k_rope,
                               int n_h, mla_dtype dt, hipStream_t stream);
 
 /*
+ * Ordinary attention over reconstructed keys and values, the second half of
+ * the naive path ([VUP] prefill excerpt: q = [q_nope ; q_pe] per head,
+ * scores times the scale, plus the index mask of each query token and the
+ * causal mask, softmax over keys, probability-weighted values; [KVR] "How it
+ * works": the keys and values come from the reconstruction). Queries sit at
+ * the end of the keys: query s is position T - S + s (T == S for a prefill
+ * from an empty cache). For sequence b, query s < S, head h < n_h:
+ *   z[t] = scale * q[b,s,h,:] . k[b,t,h,:],  t < T
+ *   z[t] = -inf when topk_idx is given and t is not in topk_idx[b,s,0..K-1]
+ *          (one set per query token; entries outside [0, T) are ignored and
+ *          repeats count once: the set of the scatter), and when causal != 0
+ *          and t > T - S + s
+ *   out[b,s,h,:] = sum_t softmax_t(z) v[b,t,h,:];  lse[b,s,h] = log sum_t exp z
+ *   A query with no visible key gets out = 0 and lse = -inf.
+ *   q [B, S, n_h, 192], k [B, T, n_h, 192], v [B, T, n_h, 128] (the layouts
+ *   mla_kv_reconstruct writes for N = B*T tokens), out [B, S, n_h, 128] (dt),
+ *   lse [B, S, n_h] float32 or NULL, topk_idx int32 [B, S, K] or NULL.
+ *   workspace: mla_attention_naive_workspace_bytes(B, S, T, K) bytes (0, and
+ *   NULL allowed, without index sets): one bit per (query, key).
+ * Requirements: T >= 1, 1 <= K <= T with index sets, T >= S when causal.
+ */
+size_t mla_attention_naive_workspace_bytes(int B, int S, int T, int K);
+mla_status mla_attention_naive(const void* q, const void* k, const void* v, int B, int S, int T,
+                               int n_h, const int32_t* topk_idx, int K, int causal, float scale,
+                               void* out, float* lse, void* workspace, size_t ws_bytes,
+                               mla_dtype dt, hipStream_t stream);
+
+/*
  * Cache append: the new tokens' entries of the compressed cache ([KVL]
  * "Key–value down-projection": the down-projection output is split into the
  * latent and the rotary key, the latent is normalised and the key rotated;

@@ -185,6 +185,29 @@ def test_cache_append_argument_errors(lib):
     assert append(lib, N=0, kv=None, pos=None) == OK      # no rows: no-op
 
 
+def test_attention_naive_argument_errors(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, S=64, T=64, n_h=4, idx=None, K=0, causal=1,
+                 scale=0.07, out=FAKE, lse=None, ws=None, ws_bytes=0, dt=BF16, stream=None)
+        a.update(kw)
+        return lib.mla_attention_naive(a["q"], a["k"], a["v"], a["B"], a["S"], a["T"], a["n_h"],
+                                       a["idx"], a["K"], a["causal"], a["scale"], a["out"],
+                                       a["lse"], a["ws"], a["ws_bytes"], a["dt"], a["stream"])
+    assert call(q=None) == INVALID
+    assert call(T=0) == INVALID
+    assert call(S=65) == INVALID                       # causal needs T >= S
+    assert call(idx=FAKE, K=0) == INVALID
+    assert call(idx=FAKE, K=65) == INVALID
+    assert call(idx=FAKE, K=8) == WORKSPACE            # the bit mask needs a workspace
+    assert call(scale=-1.0) == INVALID
+    assert call(dt=9) == INVALID
+    assert call(q=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert call(S=0, q=None) == OK
+    ws = binding.mla_attention_naive_workspace_bytes
+    assert ws(1, 64, 64, 0) == 0
+    assert ws(1, 300, 300, 16) == 1 * 10 * 512 * 4     # 2 words per 64-key tile x padded queries
+
+
 def test_binding_requires_device_tensors():
     import torch
     with pytest.raises(ValueError):
