@@ -125,6 +125,67 @@ def cpu_baseline(cfg, inp):
                       f"fp64 C oracle, OpenMP over (sequence, head)"}
 
 
+def time_single_call(args, torch, call, R):
+    """Workloads of one library call per step. Returns (per-call ms, step ms).
+
+    Per-call duration: graphs of R and 3R back-to-back calls (one per input
+    replica), the difference divided by 2R, which cancels the fixed cost of
+    launching a graph; with --no-graph, events around eager launches.
+    Timed region: exactly K calls bracketed by synchronisation, replayed from
+    graphs of R calls plus one graph of the K mod R rest (or launched eagerly
+    with --no-graph)."""
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    if args.no_graph:
+        e0, e1 = events()
+        e0.record()
+        for i in range(args.steps):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        return ms, ms
+
+    def graph_of(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(g, rounds):
+        e0, e1 = events()
+        e0.record()
+        for _ in range(rounds):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    g1, g3 = graph_of(R), graph_of(3 * R)
+    rounds = max(2, args.steps // (2 * R))
+    call_ms = (replay_ms(g3, rounds) - replay_ms(g1, rounds)) / (rounds * 2 * R)
+    full, rest = divmod(args.steps, R)
+    g_rest = graph_of(rest) if rest else None
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    e0.record()
+    for _ in range(full):
+        g1.replay()
+    if g_rest is not None:
+        g_rest.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return call_ms, e0.elapsed_time(e1) / args.steps
+
+
 def reconstruct_main(args, torch, mla, synth):
     """Config 5: the naive path's KV reconstruction, one call per step."""
     dev = torch.device("cuda:0")
@@ -142,20 +203,10 @@ def reconstruct_main(args, torch, mla, synth):
         x = reps[i % R]
         mla.mla_kv_reconstruct(x["c"], x["k_rope"], x["wkv_b"], K, V)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    call_ms, ms = time_single_call(args, torch, step, R)
     nbytes = (N * 512 + N * 64 + n_h * 256 * 512 + N * n_h * (192 + 128)) * 2
     flops = 2 * N * 512 * n_h * 256
-    tflops = flops / (ms * 1e-3) / 1e12
+    tflops = flops / (call_ms * 1e-3) / 1e12
     line = {
         "metric": "MLA KV reconstruction: token·heads/s and % of MFMA roofline",
         "value": N * n_h / (ms * 1e-3), "unit": "token·heads/s", "n_gpus": 1,
@@ -165,9 +216,10 @@ def reconstruct_main(args, torch, mla, synth):
         "config": {"workload": cfg["name"], "N": N, "n_h": n_h, "input_replicas": R},
         "roofline": {"bound": "mfma", "kernel": "mla_kv_reconstruct", "achieved": tflops,
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFS, "traffic": None,
+                     "frac": tflops / MFMA_BF16_PEAK_TFS,
+                     "traffic": traffic_record("reconstruct_config5"),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": ms * 1e3,
+                     "avg_launch_us": call_ms * 1e3,
                      "roofline_us": roofline_time_s(nbytes, flops) * 1e6},
         "published_baseline": "none: the source pages print no throughput figures",
     }
@@ -204,46 +256,7 @@ def append_main(args, torch, mla, synth):
         mla.mla_cache_append(x["kv_a"], x["gamma"], x["freqs"], x["pos"], cache[..., :512],
                              cache[..., 512:], seq_idx=x["seq_idx"])
 
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    def graph_of(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                call(i)
-        g.replay()
-        torch.cuda.synchronize()
-        return g
-
-    def replay_ms(g, rounds):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(rounds):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
-    g1, g3 = graph_of(R), graph_of(3 * R)
-    rounds = max(2, args.steps // (2 * R))
-    call_ms = (replay_ms(g3, rounds) - replay_ms(g1, rounds)) / (rounds * 2 * R)
-    # timed region: exactly K calls, graphs of R calls plus a remainder graph
-    full, rest = divmod(args.steps, R)
-    g_rest = graph_of(rest) if rest else None
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(full):
-        g1.replay()
-    if g_rest is not None:
-        g_rest.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    call_ms, ms = time_single_call(args, torch, call, R)
     # algorithmic bytes per row: 576 bf16 in, 576 bf16 out, the 256-byte
     # (cos, sin) table row, two int32 indices; plus the 2 KB gain once
     nbytes = N * (576 * 2 * 2 + 256 + 8) + 512 * 4
@@ -293,45 +306,7 @@ def attention_main(args, torch, mla, synth):
         x = reps[i % R]
         mla.mla_attention_naive(x["q"], x["k"], x["v"], causal=True, out=out)
 
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    def graph_of(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                call(i)
-        g.replay()
-        torch.cuda.synchronize()
-        return g
-
-    def replay_ms(g, rounds):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(rounds):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
-    g1, g3 = graph_of(R), graph_of(3 * R)
-    rounds = max(2, args.steps // (2 * R))
-    call_ms = (replay_ms(g3, rounds) - replay_ms(g1, rounds)) / (rounds * 2 * R)
-    full, rest = divmod(args.steps, R)
-    g_rest = graph_of(rest) if rest else None
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(full):
-        g1.replay()
-    if g_rest is not None:
-        g_rest.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    call_ms, ms = time_single_call(args, torch, call, R)
     # algorithmic work: every visible (query, key) pair once, 192-deep score
     # and 128-deep value product per head; bytes: q, k, v in, out out
     pairs = S * (S + 1) // 2 if S == T else S * T
@@ -349,7 +324,8 @@ def attention_main(args, torch, mla, synth):
                    "B": B, "S": S, "T": T, "n_h": n_h, "input_replicas": R},
         "roofline": {"bound": "mfma", "kernel": "mla_attention_naive", "achieved": tfs,
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": tfs / MFMA_BF16_PEAK_TFS, "traffic": None,
+                     "frac": tfs / MFMA_BF16_PEAK_TFS,
+                     "traffic": traffic_record("attention_config7"),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": call_ms * 1e3,
                      "roofline_us": roofline_time_s(nbytes, flops) * 1e6},
