@@ -5,115 +5,127 @@
 //   q_lat[b,h,c] = sum_{d<128} q_nope[b,h,d] * wkv_b[h*256 + d, c]
 //
 // Per head this is a [B x 128] x [128 x 512] product; the 16 MiB of W^UK
-// (n_h = 128, bf16) dominates the bytes, so the kernel is built to have all
-// of W in flight at once and keep the contraction on MFMA.
+// (n_h = 128, bf16) dominates the bytes.
 //
-// bf16 path: one workgroup of 4 waves per (head, 128-column quarter, 32-row
-// batch tile); wave w takes the content features d in [32w, 32w+32) (two
-// k-steps of v_mfma_f32_32x32x16_bf16 with M = batch rows, N = latent
-// columns) and issues all of its loads before the first multiply. The
-// contraction runs along W's row axis (its stride), so each lane loads 8
-// consecutive W rows x 4 consecutive columns (8-byte loads) per k-step and
-// transposes that 8x4 block in registers into the B operands of four
-// N-tiles; tile j's column n is latent column 4n + j, which makes each
-// lane's four accumulators four adjacent output columns. The four partial
-// sums meet in LDS and wave 0 stores 8-byte rows.
+// bf16 path: one workgroup of 4 waves per (head, 128-column quarter). The
+// workgroup's 128 x 128 block of W^UK (32 KB) is staged into LDS with
+// 16-byte LDS-DMA loads (whole 256-byte row segments) and read back
+// transposed with ds_read_b64_tr_b16, so W is fetched once, in full lines,
+// whatever the batch size. Wave w owns latent columns 32w..32w+31 of the
+// quarter and computes the transposed product
+//   q_lat^T[32 columns x 32 rows] = W^T[columns x d] . q_nope^T[d x rows]
+// (8 k-steps of v_mfma_f32_32x32x16_bf16 per 32-row batch tile; A = W^T from
+// LDS, held in registers across batch tiles; B = 16-byte loads of q_nope
+// rows). The column order tau makes accumulator r of lane half g column
+// 16g + r, so every lane stores 32 contiguous bytes. LDS rows are
+// XOR-swizzled by 4 * (row mod 4) chunks, which keeps the transposing reads
+// free of bank conflicts.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 
-__device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
+namespace {
+
+constexpr int AB_ROW_BYTES = 256;                  // 128 columns of bf16
+constexpr int AB_BYTES = D_N * AB_ROW_BYTES;       // 32 KiB staged block
+constexpr int AB_DMA = AB_BYTES / 1024 / 4;        // 8 wave-DMAs per wave
+
+__device__ __forceinline__ int ab_tau(int beta) { return 4 * (beta & 1) + (beta >> 1); }
+
+typedef __attribute__((address_space(3))) shortx4 ab_lds_shortx4;
+
+__device__ __forceinline__ bf16x8 ab_tr_pair(const char* lo, const char* hi) {
+  const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ab_lds_shortx4*)(lo));
+  const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ab_lds_shortx4*)(hi));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
-__device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
-}
+
+}  // namespace
 
 __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ w,
                                                             uint16_t* __restrict__ q_lat, int B,
                                                             int n_h) {
-  __shared__ __attribute__((aligned(16))) floatx4 red[3][4][4][64];  // waves 1..3 partials
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) char wl[AB_BYTES];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int nbt = (B + 31) >> 5;
   // Workgroups are dealt to the 8 XCDs round-robin in launch order; when the
   // heads split evenly, XCD x takes every workgroup of heads h = x (mod 8),
   // so the four quarters of each weight row are fetched by one XCD.
   int L = blockIdx.x;
   if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (static_cast<int>(gridDim.x) >> 3);
-  const int bt = L % nbt;
-  const int cq = (L / nbt) & 3;
-  const int hh = L / (nbt * 4);  // head index in XCD-grouped order
+  const int cq = L & 3;
+  const int hh = L >> 2;  // head index in XCD-grouped order
   const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
-  // rows past B load row B-1 (unconditional loads keep all of them in
-  // flight); their results are never stored
-  const int b = min(bt * 32 + n, B - 1);  // this lane's A-operand row
-  const int col0 = cq * 128 + 4 * n;
-  const uint16_t* wh = w + static_cast<int64_t>(h) * ROWS_PER_HEAD * D_C + col0;
-  const uint16_t* qrow = q_nope + (static_cast<int64_t>(b) * n_h + h) * D_N;
 
-  // all loads of this wave up front: 2 k-steps x (A: 16 bytes, B: 8 rows x 8 bytes)
-  u32x4 a[2];
-  u32x2 e[2][8];
+  // stage W^UK[h][0..127][128cq .. 128cq+127]: slot q of the block is row
+  // q/16, chunk position q%16, holding global chunk position ^ 4*(row%4)
+  {
+    const i32x4 rs = make_rsrc(w + static_cast<int64_t>(h) * ROWS_PER_HEAD * D_C + cq * 128);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wl));
 #pragma unroll
-  for (int k = 0; k < 2; k++) {
-    const int d0 = wave * 32 + k * 16 + g * 8;
-    a[k] = ld16(qrow + d0);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      e[k][i] = *reinterpret_cast<const u32x2*>(wh + static_cast<int64_t>(d0 + i) * D_C);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load issued before the first wait
-  floatx16 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) acc[j] = floatx16{};
-#pragma unroll
-  for (int k = 0; k < 2; k++) {
-    // e[k][i] holds W[d0+i][col0 .. col0+3]; operand j needs W[d0..d0+7][col0+j]
-    u32x4 bj[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      bj[0][r] = lo_lo(e[k][2 * r][0], e[k][2 * r + 1][0]);
-      bj[1][r] = hi_hi(e[k][2 * r][0], e[k][2 * r + 1][0]);
-      bj[2][r] = lo_lo(e[k][2 * r][1], e[k][2 * r + 1][1]);
-      bj[3][r] = hi_hi(e[k][2 * r][1], e[k][2 * r + 1][1]);
+    for (int j = 0; j < AB_DMA; j++) {
+      const int q = (wave + 4 * j) * 64 + lane;
+      const int r = q >> 4, pos = q & 15;
+      const int c = pos ^ (4 * (r & 3));
+      dma16(rs, dst + (wave + 4 * j) * 1024, static_cast<uint32_t>(r * D_C * 2 + c * 16), 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[j] = mfma32x32x16(as_bf16x8(a[k]), as_bf16x8(bj[j]), acc[j]);
   }
-  if (wave > 0) {
+  // q_nope rows of the first batch tile (rows past B re-read row B-1)
+  const int nbt = (B + 31) >> 5;
+  auto load_q = [&](int bt, u32x4* qv) {
+    const int b = min(bt * 32 + n, B - 1);
+    const uint16_t* qrow = q_nope + (static_cast<int64_t>(b) * n_h + h) * D_N + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++)
-        red[wave - 1][j][q4][lane] = floatx4{acc[j][4 * q4], acc[j][4 * q4 + 1],
-                                             acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
-  }
+    for (int ks = 0; ks < 8; ks++) qv[ks] = ld16(qrow + 16 * ks);
+  };
+  u32x4 qv[8];
+  load_q(0, qv);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (wave != 0) return;
+
+  // A operands: W^T rows = columns 32*wave + 4*tau(4a + (jj>>2)) + (jj&3),
+  // k = d rows 16ks + 8g + 0..7 (lo: +0..3, hi: +4..7)
+  bf16x8 A[8];
+  {
+    const int jj = lane & 15, a = (lane >> 4) & 1;
+    const int tau = ab_tau(4 * a + (jj & 3));
+    const int r = 8 * g + (jj >> 2);
+    const int off = r * AB_ROW_BYTES + 16 * ((4 * wave + (tau >> 1)) ^ (4 * (jj >> 2))) +
+                    8 * (tau & 1);
 #pragma unroll
-  for (int wv = 0; wv < 3; wv++)
+    for (int ks = 0; ks < 8; ks++) {
+      const char* lo = wl + off + 16 * ks * AB_ROW_BYTES;
+      A[ks] = ab_tr_pair(lo, lo + 4 * AB_ROW_BYTES);
+    }
+  }
+  const int col = cq * 128 + 32 * wave + 16 * g;  // first of this lane's 16 output columns
+  for (int bt = 0; bt < nbt; bt++) {
+    // next tile's rows into a second register set, issued before the
+    // multiplies: no branch between the multiplies and the reads of their
+    // accumulators
+    u32x4 qn[8];
+    if (bt + 1 < nbt) load_q(bt + 1, qn);
+    floatx16 acc = floatx16{};
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int ks = 0; ks < 8; ks++) acc = mfma32x32x16(A[ks], as_bf16x8(qv[ks]), acc);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        const floatx4 v = red[wv][j][q4][lane];
-        acc[j][4 * q4] += v[0];
-        acc[j][4 * q4 + 1] += v[1];
-        acc[j][4 * q4 + 2] += v[2];
-        acc[j][4 * q4 + 3] += v[3];
+    for (int ks = 0; ks < 8; ks++) qv[ks] = qn[ks];
+    const int b = bt * 32 + n;
+    if (b < B) {
+      uint16_t* dst = q_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + col;
+      u32x4 v0, v1;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v0[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        v1[i] = pack_bf16x2(acc[8 + 2 * i], acc[8 + 2 * i + 1]);
       }
-  // accumulator r of lane (n, g) is batch row 8*(r/4) + 4*g + r%4, column col0 + j
-#pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int bo = bt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (bo < B) {
-      u32x2 v;
-      v[0] = pack_bf16x2(acc[0][r], acc[1][r]);
-      v[1] = pack_bf16x2(acc[2][r], acc[3][r]);
-      *reinterpret_cast<u32x2*>(q_lat + (static_cast<int64_t>(bo) * n_h + h) * D_C + col0) = v;
+      st16(dst, v0);
+      st16(dst + 8, v1);
     }
   }
 }
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(256) void absorb_q_f32_kernel(const float* __restri
 hipError_t launch_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, int B, int n_h,
                            bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int blocks = n_h * 4 * ((B + 31) / 32);
+    const int blocks = n_h * 4;
     hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(wkv_b),
                        static_cast<uint16_t*>(q_lat), B, n_h);

@@ -9,10 +9,11 @@
 // Per head a [B x 512] x [512 x 128] product bound by streaming the 16 MiB of
 // W^UV. Here the contraction runs along W's contiguous axis, so both MFMA
 // operands are straight 16-byte loads. One workgroup of 4 waves per (head,
-// 32-wide value tile, 32-row batch tile); wave w takes latent features
-// [128w, 128w+128) (8 k-steps of v_mfma_f32_32x32x16_bf16 with M = batch
-// rows, N = value features) and issues all 16 of its loads before the first
-// multiply; the four partial sums meet in LDS.
+// 32-wide value tile); wave w takes latent features [128w, 128w+128) (8
+// k-steps of v_mfma_f32_32x32x16_bf16 with M = batch rows, N = value
+// features), keeps its W operands in registers across the 32-row batch
+// tiles (W is read once whatever the batch), and issues all loads before
+// the first multiply; the four partial sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,56 +26,68 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) floatx4 red[3][4][64];  // waves 1..3 partials
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int nbt = (B + 31) >> 5;
   // Workgroups are dealt to the 8 XCDs round-robin in launch order; when the
   // heads split evenly, XCD x takes every workgroup of heads h = x (mod 8),
-  // so the four quarters of each weight row are fetched by one XCD.
+  // so the four value tiles of each head are fetched by one XCD.
   int L = blockIdx.x;
   if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (static_cast<int>(gridDim.x) >> 3);
-  const int bt = L % nbt;
-  const int dt = (L / nbt) & 3;
-  const int hh = L / (nbt * 4);  // head index in XCD-grouped order
+  const int dt = L & 3;
+  const int hh = L >> 2;  // head index in XCD-grouped order
   const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
-  // rows past B load row B-1 (unconditional loads keep all 16 in flight);
-  // their results are never stored
-  const int b = min(bt * 32 + n, B - 1);
   const int d = dt * 32 + n;  // this lane's B-operand column (value feature)
-  const uint16_t* orow = o_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + wave * 128 + g * 8;
   const uint16_t* wrow =
       w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C + wave * 128 + g * 8;
-
+  // rows past B load row B-1 (unconditional loads keep all of them in
+  // flight); their results are never stored
+  auto load_o = [&](int bt, u32x4* a) {
+    const int b = min(bt * 32 + n, B - 1);
+    const uint16_t* orow = o_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + wave * 128 + g * 8;
+#pragma unroll
+    for (int k = 0; k < 8; k++) a[k] = ld16(orow + 16 * k);
+  };
+  // the W^UV operands stay in registers for every batch tile
   u32x4 a[8], bw[8];
+  load_o(0, a);
 #pragma unroll
-  for (int k = 0; k < 8; k++) {
-    a[k] = ld16(orow + 16 * k);
-    bw[k] = ld16(wrow + 16 * k);
-  }
+  for (int k = 0; k < 8; k++) bw[k] = ld16(wrow + 16 * k);
   __builtin_amdgcn_sched_barrier(0);  // keep every load issued before the first wait
-  floatx16 acc = {};
+  const int nbt = (B + 31) >> 5;
+  for (int bt = 0; bt < nbt; bt++) {
+    // next tile's rows into a second register set, issued before the
+    // multiplies: a branch between the multiplies and the reads of their
+    // accumulators has let an accumulator be read before the MFMA wrote it
+    u32x4 an[8];
+    if (bt + 1 < nbt) load_o(bt + 1, an);
+    floatx16 acc = {};
 #pragma unroll
-  for (int k = 0; k < 8; k++) acc = mfma32x32x16(as_bf16x8(a[k]), as_bf16x8(bw[k]), acc);
-  if (wave > 0) {
+    for (int k = 0; k < 8; k++) acc = mfma32x32x16(as_bf16x8(a[k]), as_bf16x8(bw[k]), acc);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; q4++)
-      red[wave - 1][q4][lane] =
-          floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
-  }
-  __syncthreads();
-  if (wave != 0) return;
+    for (int k = 0; k < 8; k++) a[k] = an[k];
+    if (bt > 0) __syncthreads();  // wave 0 done reading the previous tile's partials
+    if (wave > 0) {
 #pragma unroll
-  for (int wv = 0; wv < 3; wv++)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) {
-      const floatx4 v = red[wv][q4][lane];
-      acc[4 * q4] += v[0];
-      acc[4 * q4 + 1] += v[1];
-      acc[4 * q4 + 2] += v[2];
-      acc[4 * q4 + 3] += v[3];
+      for (int q4 = 0; q4 < 4; q4++)
+        red[wave - 1][q4][lane] =
+            floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
     }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int bo = bt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (bo < B) out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(acc[r]);
+      for (int wv = 0; wv < 3; wv++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const floatx4 v = red[wv][q4][lane];
+          acc[4 * q4] += v[0];
+          acc[4 * q4 + 1] += v[1];
+          acc[4 * q4 + 2] += v[2];
+          acc[4 * q4 + 3] += v[3];
+        }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int bo = bt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (bo < B) out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(acc[r]);
+      }
+    }
   }
 }
 
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(128) void out_up_f32_kernel(const float* __restrict
 hipError_t launch_out_up(const void* o_lat, const void* wkv_b, void* out, int B, int n_h,
                          bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int blocks = n_h * 4 * ((B + 31) / 32);
+    const int blocks = n_h * 4;
     hipLaunchKernelGGL(out_up_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(wkv_b),
                        static_cast<uint16_t*>(out), B, n_h);
