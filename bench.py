@@ -1,16 +1,20 @@
 """Benchmark of the absorbed MLA decode step on one MI355X.
 
 One step = the whole hot path on one batch of synthetic input already resident
-in HBM: mla_absorb_q -> mla_decode_latent_attn -> mla_out_up (plus, for the
-fp8 sparse workload, the weights are dequantised once before timing, as the
-method memoises them). Default workload: B=32, n_h=128, T=4096 cached
-positions, bf16, 1 query token per sequence.
+in HBM: absorb W^UK, latent attention (split over positions), merge of the
+splits, W^UV — by default the one call mla_decode_step, which fuses the split
+merge into W^UV; with --three-calls the separate calls mla_absorb_q ->
+mla_decode_latent_attn -> mla_out_up. For the fp8 sparse workload the weights
+are dequantised once before timing, as the method memoises them. Default
+workload: B=32, n_h=128, T=4096 cached positions, bf16, 1 query token per
+sequence.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
-synchronisation, HIP events on the stream the kernels run on. Each step uses
-the next of R device replicas of the inputs (>= 1 GiB in total) so the
-256 MB Infinity Cache cannot serve the cache reads. Per-call durations come
-from events around each call inside the timed region.
+synchronisation, HIP events on the stream the kernels run on, replayed from
+HIP graphs of R steps. Each step uses the next of R device replicas of the
+inputs (>= 1 GiB in total) so the 256 MB Infinity Cache cannot serve the
+cache reads. The roofline object reports the stand-alone attention call
+(split + merge kernels), timed per call from graphs of R and 3R calls.
 
 Prints ONE JSON line (metric/value/unit/..., roofline, cpu_baseline).
 """
@@ -44,6 +48,9 @@ def parse():
                          "causal attention over reconstructed K/V, S=T=8192, 128 heads")
     ap.add_argument("--min-replica-bytes", type=float, default=1.1e9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--three-calls", action="store_true",
+                    help="run the decode step as three library calls (absorb, attention with "
+                         "its split merge, W^UV) instead of the one-call mla_decode_step")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--tp", type=int, default=1, metavar="G",
@@ -414,36 +421,38 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     splits = mla.mla_decode_num_splits(B, n_h, T, K)
 
+    step_ws_bytes = mla.mla_decode_step_workspace_bytes(B, 1, n_h, T, K, 0)
+    step_ws = torch.empty(max(step_ws_bytes, 1), dtype=torch.uint8, device=dev)
+
     def step(r, ev=None):
         x = reps[r % R]
         if ev is not None:
             ev[0].record()
-        mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
+        if args.three_calls:
+            mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
+            mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
+                                       x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
+                                       out_lat=o_lat, workspace=ws)
+            mla.mla_out_up(o_lat, x["w"], out)
+        else:
+            # one call: absorb, split attention, split merge fused into W^UV
+            mla.mla_decode_step(x["q_nope"], x["q_pe"], x["w"], x["cache"][..., :512],
+                                x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
+                                out=out, workspace=step_ws)
         if ev is not None:
             ev[1].record()
-        mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
-                                   x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
-                                   out_lat=o_lat, workspace=ws)
-        if ev is not None:
-            ev[2].record()
-        mla.mla_out_up(o_lat, x["w"], out)
-        if ev is not None:
-            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # eager pass: events around each call
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # eager pass: events around each step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    absorb_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    outup_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    eager_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    eager_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
 
     # per-call durations without host launch overhead: one HIP graph per call
     # kind holding that call once per replica, replayed; events on the stream
@@ -488,7 +497,22 @@ def main():
         rounds = max(2, args.steps // (2 * R))
         return (replay_ms(g3, rounds) - replay_ms(g1, rounds)) / (rounds * 2 * R)
 
-    if not args.no_graph:
+    if args.no_graph:
+        # eager launches with events around each call (counter runs see
+        # every dispatch)
+        def eager_call_ms(fn):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                fn(i % R)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+        absorb_ms = eager_call_ms(call_absorb)
+        decode_ms = eager_call_ms(call_decode)
+        outup_ms = eager_call_ms(call_out_up)
+    else:
         absorb_ms = graph_call_ms(call_absorb)
         decode_ms = graph_call_ms(call_decode)
         outup_ms = graph_call_ms(call_out_up)
@@ -554,6 +578,9 @@ def main():
                  "GB_s": work["step_bytes"] / (ms_step * 1e-3) / 1e9,
                  "TFLOP_s": work["step_flops"] / (ms_step * 1e-3) / 1e12,
                  "launch": "eager" if args.no_graph else f"hip_graph_replay ({R} steps per graph)",
+                 "path": ("three calls: mla_absorb_q, mla_decode_latent_attn, mla_out_up"
+                          if args.three_calls else
+                          "mla_decode_step: absorb, split attention, split merge fused into W^UV"),
                  "eager_step_us": eager_ms * 1e3,
                  "absorb_us": absorb_ms * 1e3, "decode_us": decode_ms * 1e3,
                  "out_up_us": outup_ms * 1e3},

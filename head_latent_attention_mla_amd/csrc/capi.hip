@@ -354,6 +354,14 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
   st = from_hip(launch_absorb_q(q_nope, wkv_b, q_lat, BS, n_h, dt == MLA_BF16, stream),
                 "absorb launch");
   if (st != MLA_OK) return st;
+  if (dt == MLA_BF16 && p.num_splits > 1) {
+    // the split merge is fused into W^UV: the merged rows stay on chip
+    st = from_hip(launch_decode(p, true, stream, false), "decode launch");
+    if (st != MLA_OK) return st;
+    return from_hip(launch_merge_out_up(p.ws_o, p.ws_lse, p.num_splits, wkv_b, out, lse, BS, n_h,
+                                        stream),
+                    "merge_out_up launch");
+  }
   st = from_hip(launch_decode(p, dt == MLA_BF16, stream), "decode launch");
   if (st != MLA_OK) return st;
   return from_hip(launch_out_up(o_lat, wkv_b, out, BS, n_h, dt == MLA_BF16, stream),

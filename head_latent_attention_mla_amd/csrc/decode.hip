@@ -42,6 +42,7 @@
 // float32 interface (a correctness path, not a performance path).
 #include "common.hpp"
 #include "launch.hpp"
+#include "merge.hpp"
 
 namespace mla {
 
@@ -625,11 +626,7 @@ __global__ __launch_bounds__(64) void merge_splits_f32_kernel(const T* __restric
 }
 
 // bf16 partials: 64 lanes per (b, h) row, 8 latent features (16 bytes) per
-// lane, four rows per workgroup. Splits are taken MERGE_CHUNK at a time; a
-// chunk's log-sum-exps and partials are loaded together (one memory round
-// trip per chunk: indices past the last split are clamped and weighted
-// zero) and folded in with a running maximum.
-constexpr int MERGE_CHUNK = 8;
+// lane, four rows per workgroup (the per-row arithmetic is merge_rows8).
 __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_lse,
                                                                 int S, int64_t BH,
@@ -638,42 +635,13 @@ __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* 
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
   const int c0 = (threadIdx.x & 63) * 8;
-  float mx = -INFINITY, wsum = 0.f;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
-    u32x4 v[MERGE_CHUNK];
-    float lv[MERGE_CHUNK];
-#pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; j++) {
-      const int64_t sj = min(s0 + j, S - 1);
-      lv[j] = ws_lse[sj * BH + bh];
-      v[j] = ld16(ws_o + (sj * BH + bh) * D_C + c0);
-    }
-    float cm = mx;
-#pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; j++) cm = fmaxf(cm, lv[j]);
-    const float f = __expf(mx - cm);  // 0 on the first chunk (mx = -inf)
-    wsum *= f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] *= f;
-    mx = cm;
-#pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; j++) {
-      const float w = s0 + j < S ? __expf(lv[j] - mx) : 0.f;
-      wsum += w;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        acc[2 * i] = fmaf(w, __uint_as_float(v[j][i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, __uint_as_float(v[j][i] & 0xFFFF0000u), acc[2 * i + 1]);
-      }
-    }
-  }
-  const float inv = 1.f / wsum;
+  float o8[1][8], l;
+  merge_rows8<1>(ws_o, ws_lse, S, BH, &bh, c0, o8, &l);
   u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; i++) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  for (int i = 0; i < 4; i++) o[i] = pack_bf16x2(o8[0][2 * i], o8[0][2 * i + 1]);
   st16(out + bh * D_C + c0, o);
-  if ((threadIdx.x & 63) == 0 && lse) lse[bh] = mx + logf(wsum);
+  if ((threadIdx.x & 63) == 0 && lse) lse[bh] = l;
 }
 
 // ---------------------------------------------------------------------------
@@ -757,7 +725,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
   if (tid == 0 && lse_dst) *lse_dst = m + logf(l);
 }
 
-hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream,
+                         bool merge_splits) {
   const int hgroups = (p.n_h + 127) / 128;
   if (is_bf16) {
     dim3 grid(p.num_splits, hgroups, p.B);
@@ -772,7 +741,7 @@ hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream
     hipLaunchKernelGGL(decode_f32_kernel, dim3(p.num_splits, p.n_h, p.B), dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_splits == 1) return e;
+  if (e != hipSuccess || p.num_splits == 1 || !merge_splits) return e;
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
   if (is_bf16)
     hipLaunchKernelGGL(merge_splits_bf16_kernel, dim3(static_cast<unsigned>((BH + 3) / 4)),

@@ -40,7 +40,15 @@ struct DecodeParams {
   float* ws_lse;       // [num_splits, B, n_h]
 };
 
-hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream);
+// merge_splits = false leaves the split partials in the workspace (for
+// launch_merge_out_up)
+hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream,
+                         bool merge_splits = true);
+
+// bf16 only: merge of S split partials ([S][B*n_h][512] + [S][B*n_h] lse)
+// fused with W^UV; out [B, n_h, 128], lse [B*n_h] or nullptr
+hipError_t launch_merge_out_up(const void* ws_o, const float* ws_lse, int S, const void* wkv_b,
+                               void* out, float* lse, int B, int n_h, hipStream_t stream);
 
 struct AppendParams {
   const void* kv_a;      // [N, in_rstride]: 512 latent then 64 rotary features

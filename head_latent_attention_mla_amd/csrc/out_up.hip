@@ -16,6 +16,7 @@
 // the first multiply; the four partial sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
+#include "merge.hpp"
 
 namespace mla {
 
@@ -89,6 +90,123 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
       }
     }
   }
+}
+
+// Merge of the decode's split partials fused with W^UV (the one-call decode
+// step): one workgroup of 8 waves per (head, 16-row batch tile), so a
+// 32-row batch gives two workgroups per head and the chip is filled. The
+// waves first merge the tile's rows (wave w: rows w and w+8, both loaded in
+// one memory round trip; lane: 8 latent features, the arithmetic of the
+// stand-alone merge) into a bf16 o_lat tile in LDS, then wave (dt, kh)
+// multiplies it by value features 32dt..32dt+31 of W^UV over latent half kh
+// (two 128-feature quarters; its W operands were loaded before the merge)
+// and the partial sums meet in LDS, added in the stand-alone kernel's
+// order. The merged rows never go to memory; the result has the bits of
+// merge + out-up. The MFMA tile has 32 rows: rows 16..31 repeat 0..15 and
+// are not stored. LDS rows are XOR-swizzled by (row mod 16) chunks so the
+// 16 rows of an operand read hit distinct banks.
+constexpr int MO_ROWS = 16;
+__global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
+    const uint16_t* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
+    const uint16_t* __restrict__ w, uint16_t* __restrict__ out, float* __restrict__ lse, int B,
+    int n_h) {
+  __shared__ __attribute__((aligned(16))) char ol[MO_ROWS * D_C * 2];   // merged rows
+  __shared__ __attribute__((aligned(16))) floatx4 red[2][4][2][64];     // kh = 1 quarter sums
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int nbt = (B + MO_ROWS - 1) / MO_ROWS;
+  // the batch tiles of eight consecutive heads share an XCD (as in out-up)
+  int L = blockIdx.x;
+  const int G = gridDim.x;
+  if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (G >> 3);
+  const int bt = L % nbt;
+  const int hh = L / nbt;
+  const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
+  const int dt = wave & 3, kh = wave >> 2;
+  const int d = dt * 32 + n;
+
+  u32x4 bw[16];
+  {
+    const uint16_t* wrow =
+        w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C + kh * 256 + g * 8;
+#pragma unroll
+    for (int k = 0; k < 16; k++) bw[k] = ld16(wrow + 16 * k);
+  }
+  const int64_t BH = static_cast<int64_t>(B) * n_h;
+  {
+    // rows wave and wave + 8 of the tile (rows past B merge row B-1 and are
+    // never stored)
+    int64_t bh[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+      bh[i] = static_cast<int64_t>(min(bt * MO_ROWS + wave + 8 * i, B - 1)) * n_h + h;
+    float o8[2][8], l[2];
+    merge_rows8<2>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int r = wave + 8 * i;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(o8[i][2 * q], o8[i][2 * q + 1]);
+      *reinterpret_cast<u32x4*>(ol + r * (D_C * 2) + 16 * (lane ^ r)) = o;
+      if (lane == 0 && lse && bt * MO_ROWS + r < B) lse[bh[i]] = l[i];
+    }
+  }
+  __syncthreads();
+  // two 128-feature quarters per wave, summed in the order the stand-alone
+  // W^UV kernel uses ((q0 + q1) + q2) + q3, so both paths give the same bits
+  floatx16 acc[2] = {floatx16{}, floatx16{}};
+  {
+    const int r = n & 15;
+    const char* arow = ol + r * (D_C * 2);
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      const int c = kh * 32 + 2 * k + g;
+      const u32x4 a = ld_lds16(arow + 16 * (c ^ r));
+      acc[k >> 3] = mfma32x32x16(as_bf16x8(a), as_bf16x8(bw[k]), acc[k >> 3]);
+    }
+  }
+  // accumulators 0..7 of lane half g hold rows 8*(r/4) + 4g + r%4 < 16
+  if (kh == 1) {
+#pragma unroll
+    for (int qq = 0; qq < 2; qq++)
+#pragma unroll
+      for (int q4 = 0; q4 < 2; q4++)
+        red[qq][dt][q4][lane] = floatx4{acc[qq][4 * q4], acc[qq][4 * q4 + 1],
+                                        acc[qq][4 * q4 + 2], acc[qq][4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float sum[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) sum[i] = acc[0][i] + acc[1][i];
+#pragma unroll
+    for (int qq = 0; qq < 2; qq++)
+#pragma unroll
+      for (int q4 = 0; q4 < 2; q4++) {
+        const floatx4 v = red[qq][dt][q4][lane];
+        sum[4 * q4] += v[0];
+        sum[4 * q4 + 1] += v[1];
+        sum[4 * q4 + 2] += v[2];
+        sum[4 * q4 + 3] += v[3];
+      }
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const int bo = bt * MO_ROWS + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (bo < B) out[(static_cast<int64_t>(bo) * n_h + h) * D_V + d] = float_to_bf16_bits(sum[r]);
+    }
+  }
+}
+
+hipError_t launch_merge_out_up(const void* ws_o, const float* ws_lse, int S, const void* wkv_b,
+                               void* out, float* lse, int B, int n_h, hipStream_t stream) {
+  const int blocks = n_h * ((B + MO_ROWS - 1) / MO_ROWS);
+  hipLaunchKernelGGL(merge_out_up_bf16_kernel, dim3(blocks), dim3(512), 0, stream,
+                     static_cast<const uint16_t*>(ws_o), ws_lse, S,
+                     static_cast<const uint16_t*>(wkv_b), static_cast<uint16_t*>(out), lse, B,
+                     n_h);
+  return hipGetLastError();
 }
 
 // fp32: one block per (b, h); thread d walks its W^UV row.
