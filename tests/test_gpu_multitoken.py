@@ -152,3 +152,25 @@ def test_decode_step_causal_pair_at_decode_workload_size_sampled():
     sel = [0, 17, 31]
     ref, _ = oracle_step(inp, True, sel=sel)
     check(f64(out.cpu()[sel]), ref, TOL[torch.bfloat16], "out")
+
+
+@pytest.mark.parametrize("B,S_q,n_h,T", [(33, 1, 128, 700), (3, 2, 16, 900), (5, 1, 20, 2000),
+                                         (17, 1, 96, 300)])
+def test_decode_step_fused_merge_matches_the_separate_kernels(B, S_q, n_h, T):
+    # with several splits the one-call step merges them inside W^UV; the
+    # result must have exactly the bits of attention (with its merge) + W^UV
+    inp = multi_inputs(B, S_q, n_h, T, torch.bfloat16, seed=B * 7 + n_h + T)
+    assert mla.mla_decode_num_splits(B, S_q * n_h, T) > 1
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    cache = d["cache"]
+    one, lse1 = mla.mla_decode_step(d["q_nope"], d["q_pe"], d["wkv_b"], cache[..., :512],
+                                    cache[..., 512:], causal=S_q > 1, want_lse=True)
+    BS = B * S_q
+    q_lat = mla.mla_absorb_q(d["q_nope"].reshape(BS, n_h, 128), d["wkv_b"])
+    o_lat, lse3 = mla.mla_decode_latent_attn_multi(q_lat.reshape(B, S_q, n_h, 512), d["q_pe"],
+                                                   cache[..., :512], cache[..., 512:],
+                                                   causal=S_q > 1, want_lse=True)
+    three = mla.mla_out_up(o_lat.reshape(BS, n_h, 512), d["wkv_b"]).reshape(B, S_q, n_h, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu().view(torch.int16), three.cpu().view(torch.int16))
+    assert torch.equal(lse1.cpu(), lse3.cpu())
