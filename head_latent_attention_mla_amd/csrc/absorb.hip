@@ -45,22 +45,29 @@ __device__ __forceinline__ bf16x8 ab_tr_pair(const char* lo, const char* hi) {
 
 }  // namespace
 
+// swz_sq = 0: q_lat rows [B, n_h, 512]. swz_sq = s_q > 0: the decode's
+// operand order for B / s_q sequences of s_q * n_h query rows (row j * n_h + h
+// of sequence b is batch row b * s_q + j, head h): 16-byte slot
+// ((((b * HG + hg) * 4 + hq) * 32 + ks) * 64 + g * 32 + (v & 31)) holds
+// features 16ks + 8g of query row v = hg * 128 + hq * 32 + (v & 31),
+// HG = s_q * n_h / 128.
 __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ w,
                                                             uint16_t* __restrict__ q_lat, int B,
-                                                            int n_h) {
+                                                            int n_h, int swz_sq) {
   __shared__ __attribute__((aligned(16))) char wl[AB_BYTES];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
   // Workgroups are dealt to the 8 XCDs round-robin in launch order; when the
-  // heads split evenly, XCD x takes every workgroup of heads h = x (mod 8),
-  // so the four quarters of each weight row are fetched by one XCD.
+  // heads split evenly, XCD x takes the workgroups of heads
+  // [x * n_h/8, (x+1) * n_h/8): the query rows of eight consecutive heads,
+  // which share 128-byte lines in the operand-order output, are then written
+  // through one L2 and leave it as whole lines.
   int L = blockIdx.x;
   if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (static_cast<int>(gridDim.x) >> 3);
   const int cq = L & 3;
-  const int hh = L >> 2;  // head index in XCD-grouped order
-  const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
+  const int h = L >> 2;
 
   // stage W^UK[h][0..127][128cq .. 128cq+127]: slot q of the block is row
   // q/16, chunk position q%16, holding global chunk position ^ 4*(row%4)
@@ -117,15 +124,26 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
     for (int ks = 0; ks < 8; ks++) qv[ks] = qn[ks];
     const int b = bt * 32 + n;
     if (b < B) {
-      uint16_t* dst = q_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + col;
       u32x4 v0, v1;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         v0[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
         v1[i] = pack_bf16x2(acc[8 + 2 * i], acc[8 + 2 * i + 1]);
       }
-      st16(dst, v0);
-      st16(dst + 8, v1);
+      if (swz_sq == 0) {
+        uint16_t* dst = q_lat + (static_cast<int64_t>(b) * n_h + h) * D_C + col;
+        st16(dst, v0);
+        st16(dst + 8, v1);
+      } else {
+        // the lane's 16 columns are k-step col/16, both lane halves
+        const int seq = b / swz_sq;
+        const int v = (b - seq * swz_sq) * n_h + h;
+        const int hgs = swz_sq * n_h >> 7;
+        uint16_t* dst = q_lat + ((((static_cast<int64_t>(seq) * hgs + (v >> 7)) * 4 +
+                                   ((v >> 5) & 3)) * 32 + (col >> 4)) * 64 + (v & 31)) * 8;
+        st16(dst, v0);
+        st16(dst + 32 * 8, v1);
+      }
     }
   }
 }
@@ -150,12 +168,20 @@ hipError_t launch_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, i
     const int blocks = n_h * 4;
     hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(wkv_b),
-                       static_cast<uint16_t*>(q_lat), B, n_h);
+                       static_cast<uint16_t*>(q_lat), B, n_h, 0);
   } else {
     hipLaunchKernelGGL(absorb_q_f32_kernel, dim3(static_cast<unsigned>(B) * n_h * 2), dim3(256), 0,
                        stream, static_cast<const float*>(q_nope),
                        static_cast<const float*>(wkv_b), static_cast<float*>(q_lat), n_h);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_swizzled(const void* q_nope, const void* wkv_b, void* q_lat, int B,
+                                    int n_h, int s_q, hipStream_t stream) {
+  hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(n_h * 4), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(wkv_b),
+                     static_cast<uint16_t*>(q_lat), B, n_h, s_q);
   return hipGetLastError();
 }
 

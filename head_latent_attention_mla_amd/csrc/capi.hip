@@ -351,8 +351,17 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
                                  scale, num_splits, o_lat, lse, ws + 2 * lat, ws_bytes - 2 * lat,
                                  dt, &p, &empty);
   if (st != MLA_OK) return st;
-  st = from_hip(launch_absorb_q(q_nope, wkv_b, q_lat, BS, n_h, dt == MLA_BF16, stream),
-                "absorb launch");
+  // full 128-row groups: q_lat goes to the workspace in the attention
+  // kernel's operand order (each wave then loads one contiguous KiB per
+  // k-step instead of 32 row pieces)
+  if (dt == MLA_BF16 && (S_q * n_h) % 128 == 0) {
+    p.q_swz = 1;
+    st = from_hip(launch_absorb_q_swizzled(q_nope, wkv_b, q_lat, BS, n_h, S_q, stream),
+                  "absorb launch");
+  } else {
+    st = from_hip(launch_absorb_q(q_nope, wkv_b, q_lat, BS, n_h, dt == MLA_BF16, stream),
+                  "absorb launch");
+  }
   if (st != MLA_OK) return st;
   if (dt == MLA_BF16 && p.num_splits > 1) {
     // the split merge is fused into W^UV: the merged rows stay on chip

@@ -286,7 +286,18 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     m_off = row0 * LAT_PITCH + 16 * (2 * g + (tau >> 1)) + 8 * (tau & 1) + 64 * 2 * wave;
   }
   const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
-  const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
+  // this lane's query operands: k-step ks is ql[16 * ks] (rows) or
+  // ql[512 * ks] (operand order: one contiguous KiB per wave and k-step)
+  const uint16_t* ql;
+  int ql_step;
+  if (FULL && p.q_swz) {
+    ql = static_cast<const uint16_t*>(p.q_lat) +
+         ((static_cast<int64_t>(b) * (p.n_h >> 7) + hg) * 4 + hq) * (32 * 512) + 8 * lane;
+    ql_step = 512;
+  } else {
+    ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
+    ql_step = 16;
+  }
 
   floatx16 acc[2][4];  // mix accumulators [feature tile][head tile]
 #pragma unroll
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     // 8 at 16ks + 8g; rotary operands staged in LDS as [hq][k-step][lane]
     bf16x8 q[QK_P_STEPS];
 #pragma unroll
-    for (int j = 0; j < QK_P_STEPS; j++) q[j] = as_bf16x8(ld16(ql + 16 * j));
+    for (int j = 0; j < QK_P_STEPS; j++) q[j] = as_bf16x8(ld16(ql + ql_step * j));
     {
       const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R + 8 * g;
 #pragma unroll
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
     // ======== owner waves: the last QK_O_STEPS latent k-steps and the softmax ========
     bf16x8 q[QK_O_STEPS];
 #pragma unroll
-    for (int j = 0; j < QK_O_STEPS; j++) q[j] = as_bf16x8(ld16(ql + 16 * (QK_P_STEPS + j)));
+    for (int j = 0; j < QK_O_STEPS; j++) q[j] = as_bf16x8(ld16(ql + ql_step * (QK_P_STEPS + j)));
 #pragma unroll
     for (int j = 0; j < QK_O_STEPS; j++) asm volatile("" : : "v"(q[j]));
 

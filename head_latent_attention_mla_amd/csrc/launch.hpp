@@ -13,6 +13,12 @@ hipError_t launch_dequant_fp8_block(const uint8_t* w, const float* scale, int64_
 hipError_t launch_absorb_q(const void* q_nope, const void* wkv_b, void* q_lat, int B, int n_h,
                            bool is_bf16, hipStream_t stream);
 
+// bf16: q_lat written in the decode's operand order (DecodeParams::q_swz = 1)
+// for B / s_q sequences of s_q * n_h query rows each; requires
+// (s_q * n_h) % 128 == 0
+hipError_t launch_absorb_q_swizzled(const void* q_nope, const void* wkv_b, void* q_lat, int B,
+                                    int n_h, int s_q, hipStream_t stream);
+
 hipError_t launch_out_up(const void* o_lat, const void* wkv_b, void* out, int B, int n_h,
                          bool is_bf16, hipStream_t stream);
 
@@ -38,6 +44,10 @@ struct DecodeParams {
   float* lse;
   void* ws_o;          // [num_splits, B, n_h, 512] partial outputs (split > 1)
   float* ws_lse;       // [num_splits, B, n_h]
+  // q_lat layout: 0 = [B, n_h, 512] rows; 1 = operand order (full 128-row
+  // groups only): 16-byte slot ((((b * n_h/128 + hg) * 4 + hq) * 32 + ks) * 64
+  // + lane) holds row hg*128 + hq*32 + (lane & 31), features 16ks + 8*(lane >> 5)
+  int q_swz;
 };
 
 // merge_splits = false leaves the split partials in the workspace (for

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
 // step): one workgroup of 8 waves per (head, 16-row batch tile), so a
 // 32-row batch gives two workgroups per head and the chip is filled. The
 // waves first merge the tile's rows (wave w: rows w and w+8, both loaded in
-// one memory round trip; lane: 8 latent features, the arithmetic of the
-// stand-alone merge) into a bf16 o_lat tile in LDS, then wave (dt, kh)
+// one memory round trip, rows past the batch skipped; lane: 8 latent
+// features, the arithmetic of the stand-alone merge) into a bf16 o_lat tile in LDS, then wave (dt, kh)
 // multiplies it by value features 32dt..32dt+31 of W^UV over latent half kh
 // (two 128-feature quarters; its W operands were loaded before the merge)
 // and the partial sums meet in LDS, added in the stand-alone kernel's
@@ -135,22 +135,30 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
   }
   const int64_t BH = static_cast<int64_t>(B) * n_h;
   {
-    // rows wave and wave + 8 of the tile (rows past B merge row B-1 and are
-    // never stored)
-    int64_t bh[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-      bh[i] = static_cast<int64_t>(min(bt * MO_ROWS + wave + 8 * i, B - 1)) * n_h + h;
+    // rows wave and wave + 8 of the tile; rows past B are zeros in LDS (their
+    // products are never stored)
+    const int r0 = wave, r1 = wave + 8;
+    const int b0 = bt * MO_ROWS + r0, b1 = bt * MO_ROWS + r1;
     float o8[2][8], l[2];
-    merge_rows8<2>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+    int64_t bh[2] = {static_cast<int64_t>(b0) * n_h + h, static_cast<int64_t>(b1) * n_h + h};
+    int nrows = 0;
+    if (b1 < B) {
+      merge_rows8<2>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+      nrows = 2;
+    } else if (b0 < B) {
+      merge_rows8<1>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+      nrows = 1;
+    }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const int r = wave + 8 * i;
-      u32x4 o;
+      u32x4 o = u32x4{0u, 0u, 0u, 0u};
+      if (i < nrows) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(o8[i][2 * q], o8[i][2 * q + 1]);
+        for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(o8[i][2 * q], o8[i][2 * q + 1]);
+        if (lane == 0 && lse) lse[bh[i]] = l[i];
+      }
       *reinterpret_cast<u32x4*>(ol + r * (D_C * 2) + 16 * (lane ^ r)) = o;
-      if (lane == 0 && lse && bt * MO_ROWS + r < B) lse[bh[i]] = l[i];
     }
   }
   __syncthreads();
