@@ -14,7 +14,9 @@ synchronisation, HIP events on the stream the kernels run on, replayed from
 HIP graphs of R steps. Each step uses the next of R device replicas of the
 inputs (>= 1 GiB in total) so the 256 MB Infinity Cache cannot serve the
 cache reads. The roofline object reports the stand-alone attention call
-(split + merge kernels), timed per call from graphs of R and 3R calls.
+(split + merge kernels; with whole 128-head groups on the packed queries the
+step's attention kernel reads), timed per call from graphs of R and 3R
+calls.
 
 Prints ONE JSON line (metric/value/unit/..., roofline, cpu_baseline).
 """
@@ -457,15 +459,28 @@ def main():
     # per-call durations without host launch overhead: one HIP graph per call
     # kind holding that call once per replica, replayed; events on the stream
     # the graph (and so the kernels) run on
+    # whole 128-head groups: the packed (operand-order) queries the one-call
+    # step uses; the attention call is then the step's attention kernel plus
+    # the stand-alone split merge
+    packed = n_h % 128 == 0
+
     def call_absorb(r):
         x = reps[r]
-        mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
+        if packed:
+            mla.mla_absorb_q_packed(x["q_nope"], x["w"], q_lat.view(B, -1))
+        else:
+            mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
 
     def call_decode(r):
         x = reps[r]
-        mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
-                                   x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
-                                   out_lat=o_lat, workspace=ws)
+        if packed:
+            mla.mla_decode_latent_attn_packed(q_lat.view(B, -1), x["q_pe"], x["cache"][..., :512],
+                                              x["cache"][..., 512:], topk_idx=x["topk"],
+                                              scale=scale, out_lat=o_lat, workspace=ws)
+        else:
+            mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
+                                       x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
+                                       out_lat=o_lat, workspace=ws)
 
     def call_out_up(r):
         x = reps[r]
@@ -568,7 +583,9 @@ def main():
                    "attended_positions": rows, "query_tokens": 1,
                    "fp8_weights": bool(cfg.get("fp8_weights", False)),
                    "decode_splits": splits, "input_replicas": R},
-        "roofline": {"bound": "hbm", "kernel": "mla_decode_latent_attn (split + merge launches)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("mla_decode_latent_attn_packed" if packed else
+                                "mla_decode_latent_attn") + " (split + merge launches)",
                      "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": work["attn_bytes"],

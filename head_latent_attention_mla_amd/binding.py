@@ -60,6 +60,9 @@ def library() -> ctypes.CDLL:
         lib.mla_softmax_scale.restype = F
         lib.mla_decode_latent_attn_multi.argtypes = [P, P, P, P, L, L, L, L, I, I, I, I, P, I,
                                                      I, F, I, P, P, P, Z, I, P]
+        lib.mla_absorb_q_packed.argtypes = [P, P, P, I, I, I, I, P]
+        lib.mla_decode_latent_attn_packed.argtypes = [P, P, P, P, L, L, L, L, I, I, I, I, P, I,
+                                                      I, F, I, P, P, P, Z, I, P]
         lib.mla_decode_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         lib.mla_decode_step_workspace_bytes.restype = Z
         lib.mla_decode_step.argtypes = [P, P, P, P, P, L, L, L, L, I, I, I, I, P, I, I, F, I, P,
@@ -72,6 +75,7 @@ def library() -> ctypes.CDLL:
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
                      "mla_out_up", "mla_kv_reconstruct", "mla_cache_append",
                      "mla_decode_latent_attn_multi", "mla_decode_step",
+                     "mla_absorb_q_packed", "mla_decode_latent_attn_packed",
                      "mla_attention_naive"):
             getattr(lib, name).restype = I
         _lib = lib
@@ -272,6 +276,76 @@ def mla_decode_latent_attn_multi(q_lat: torch.Tensor, q_pe: torch.Tensor, latent
         _ptr(q_lat), _ptr(q_pe), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B, S_q, n_h, T,
         _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out_lat), _ptr(lse),
         _ptr(workspace), ws_bytes, _dtype_code(q_lat), _stream(stream)))
+    return (out_lat, lse) if (want_lse or lse is not None) else out_lat
+
+
+def mla_absorb_q_packed(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_packed: torch.Tensor = None,
+                        stream=None) -> torch.Tensor:
+    """Absorbed queries in the attention kernel's operand order (see
+    include/mla.h): q_nope [B, S_q, n_h, 128] (or [B, n_h, 128]) bf16 with
+    S_q * n_h a multiple of 128. Returns q_packed [B, S_q * n_h * 512]."""
+    _dev(q_nope, wkv_b, q_packed)
+    if q_nope.dim() == 3:
+        q_nope = q_nope.unsqueeze(1)
+    _require(q_nope.dim() == 4 and q_nope.shape[3] == 128 and q_nope.is_contiguous(),
+             "q_nope must be contiguous [B, S_q, n_h, 128]")
+    B, S_q, n_h, _ = q_nope.shape
+    _require(wkv_b.dtype == q_nope.dtype and wkv_b.is_contiguous() and
+             tuple(wkv_b.shape) == (n_h * 256, 512), "wkv_b must be contiguous [n_h*256, 512]")
+    if q_packed is None:
+        q_packed = torch.empty((B, S_q * n_h * 512), dtype=q_nope.dtype, device=q_nope.device)
+    _require(q_packed.dtype == q_nope.dtype and q_packed.is_contiguous() and
+             q_packed.numel() == B * S_q * n_h * 512, "q_packed must hold B*S_q*n_h*512 elements")
+    _check("mla_absorb_q_packed", library().mla_absorb_q_packed(
+        _ptr(q_nope), _ptr(wkv_b), _ptr(q_packed), B, S_q, n_h, _dtype_code(q_nope),
+        _stream(stream)))
+    return q_packed
+
+
+def mla_decode_latent_attn_packed(q_packed: torch.Tensor, q_pe: torch.Tensor,
+                                  latent: torch.Tensor, rope: torch.Tensor, T: int = None,
+                                  topk_idx: torch.Tensor = None, causal: bool = False,
+                                  scale: float = SCALE, num_splits: int = 0,
+                                  out_lat: torch.Tensor = None, lse: torch.Tensor = None,
+                                  workspace: torch.Tensor = None, want_lse: bool = False,
+                                  stream=None):
+    """mla_decode_latent_attn_multi with packed queries (mla_absorb_q_packed);
+    S_q and n_h are taken from q_pe [B, S_q, n_h, 64] (or [B, n_h, 64]).
+    Returns out_lat [B, S_q, n_h, 512] (and lse [B, S_q, n_h])."""
+    _dev(q_packed, q_pe, latent, rope, topk_idx, out_lat, lse, workspace)
+    if q_pe.dim() == 3:
+        q_pe = q_pe.unsqueeze(1)
+    _require(q_pe.dim() == 4 and q_pe.shape[3] == 64 and q_pe.is_contiguous(),
+             "q_pe must be contiguous [B, S_q, n_h, 64]")
+    B, S_q, n_h, _ = q_pe.shape
+    _require(q_packed.dtype == q_pe.dtype and q_packed.is_contiguous() and
+             q_packed.numel() == B * S_q * n_h * 512, "q_packed must hold B*S_q*n_h*512 elements")
+    _require(latent.dtype == q_pe.dtype and rope.dtype == q_pe.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    _require(latent.shape[0] >= B and rope.shape[0] >= B, "cache batch too small")
+    if T is None:
+        T = latent.shape[1]
+    _require(T <= latent.shape[1] and T <= rope.shape[1], "T exceeds the cache length")
+    K = _topk_arg(topk_idx, B)
+    if out_lat is None:
+        out_lat = torch.empty((B, S_q, n_h, 512), dtype=q_pe.dtype, device=q_pe.device)
+    _require(out_lat.dtype == q_pe.dtype and out_lat.is_contiguous() and
+             out_lat.numel() == B * S_q * n_h * 512, "out_lat must hold B*S_q*n_h*512 elements")
+    if lse is None and want_lse:
+        lse = torch.empty((B, S_q, n_h), dtype=torch.float32, device=q_pe.device)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and
+                 lse.numel() == B * S_q * n_h, "lse must be contiguous float32 [B, S_q, n_h]")
+    need = (mla_decode_workspace_bytes(B, S_q * n_h, T, K, num_splits, q_pe.dtype)
+            if B > 0 else 0)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_pe.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_latent_attn_packed", library().mla_decode_latent_attn_packed(
+        _ptr(q_packed), _ptr(q_pe), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B, S_q, n_h, T,
+        _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out_lat), _ptr(lse),
+        _ptr(workspace), ws_bytes, _dtype_code(q_pe), _stream(stream)))
     return (out_lat, lse) if (want_lse or lse is not None) else out_lat
 
 

@@ -161,7 +161,7 @@ mla_status decode_prepare(const void* q_lat, const void* q_pe, const void* laten
                           int n_h_tok, int T, const int32_t* topk_idx, int K, int causal,
                           float scale, int num_splits, void* out_lat, float* lse,
                           void* workspace, size_t ws_bytes, mla_dtype dt, DecodeParams* pp,
-                          bool* empty) {
+                          bool* empty, bool q_packed = false) {
   *empty = false;
   if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (S_q < 1) return fail(MLA_ERR_INVALID_ARG, "S_q=%d < 1", S_q);
@@ -176,6 +176,8 @@ mla_status decode_prepare(const void* q_lat, const void* q_pe, const void* laten
   if (static_cast<int64_t>(S_q) * n_h_tok > 65535)
     return fail(MLA_ERR_UNSUPPORTED, "S_q * n_h above 65535");
   const int n_h = S_q * n_h_tok;  // query rows per sequence
+  if (q_packed && (dt != MLA_BF16 || n_h % 128 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "packed queries need bf16 and S_q * n_h a multiple of 128");
   if (B == 0) {
     *empty = true;
     return MLA_OK;
@@ -241,6 +243,7 @@ mla_status decode_prepare(const void* q_lat, const void* q_pe, const void* laten
   p.num_splits = sp.num_splits;
   p.tiles_per_split = sp.tiles_per_split;
   p.scale = scale;
+  p.q_swz = q_packed ? 1 : 0;
   p.out_lat = out_lat;
   p.lse = lse;
   if (need > 0) {
@@ -257,13 +260,13 @@ mla_status decode_impl(const void* q_lat, const void* q_pe, const void* latent, 
                        int64_t rope_rstride, int B, int S_q, int n_h_tok, int T,
                        const int32_t* topk_idx, int K, int causal, float scale, int num_splits,
                        void* out_lat, float* lse, void* workspace, size_t ws_bytes,
-                       mla_dtype dt, hipStream_t stream) {
+                       mla_dtype dt, hipStream_t stream, bool q_packed = false) {
   DecodeParams p;
   bool empty;
   mla_status st = decode_prepare(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride,
                                  rope_bstride, rope_rstride, B, S_q, n_h_tok, T, topk_idx, K,
                                  causal, scale, num_splits, out_lat, lse, workspace, ws_bytes, dt,
-                                 &p, &empty);
+                                 &p, &empty, q_packed);
   if (st != MLA_OK || empty) return st;
   return from_hip(launch_decode(p, dt == MLA_BF16, stream), "decode launch");
 }
@@ -295,6 +298,36 @@ mla_status mla_decode_latent_attn_multi(const void* q_lat, const void* q_pe, con
   return decode_impl(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride, rope_bstride,
                      rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale, num_splits,
                      out_lat, lse, workspace, ws_bytes, dt, stream);
+}
+
+mla_status mla_decode_latent_attn_packed(const void* q_packed, const void* q_pe,
+                                         const void* latent, const void* rope,
+                                         int64_t lat_bstride, int64_t lat_rstride,
+                                         int64_t rope_bstride, int64_t rope_rstride, int B,
+                                         int S_q, int n_h, int T, const int32_t* topk_idx, int K,
+                                         int causal, float scale, int num_splits, void* out_lat,
+                                         float* lse, void* workspace, size_t ws_bytes,
+                                         mla_dtype dt, hipStream_t stream) {
+  return decode_impl(q_packed, q_pe, latent, rope, lat_bstride, lat_rstride, rope_bstride,
+                     rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale, num_splits,
+                     out_lat, lse, workspace, ws_bytes, dt, stream, true);
+}
+
+mla_status mla_absorb_q_packed(const void* q_nope, const void* wkv_b, void* q_packed, int B,
+                               int S_q, int n_h, mla_dtype dt, hipStream_t stream) {
+  if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 0 || S_q < 1 || n_h < 1)
+    return fail(MLA_ERR_INVALID_ARG, "B=%d S_q=%d n_h=%d", B, S_q, n_h);
+  if (dt != MLA_BF16 || (static_cast<int64_t>(S_q) * n_h) % 128 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "packed queries need bf16 and S_q * n_h a multiple of 128");
+  if (static_cast<int64_t>(B) * S_q > INT32_MAX || static_cast<int64_t>(S_q) * n_h > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "B * S_q or S_q * n_h too large");
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !wkv_b || !q_packed) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_packed))
+    return fail(MLA_ERR_UNSUPPORTED, "misaligned pointer");
+  return from_hip(launch_absorb_q_swizzled(q_nope, wkv_b, q_packed, B * S_q, n_h, S_q, stream),
+                  "absorb launch");
 }
 
 size_t mla_decode_step_workspace_bytes(int B, int S_q, int n_h, int T, int K, int num_splits,
@@ -349,13 +382,12 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
   mla_status st = decode_prepare(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride,
                                  rope_bstride, rope_rstride, B, S_q, n_h, T, topk_idx, K, causal,
                                  scale, num_splits, o_lat, lse, ws + 2 * lat, ws_bytes - 2 * lat,
-                                 dt, &p, &empty);
+                                 dt, &p, &empty, dt == MLA_BF16 && (S_q * n_h) % 128 == 0);
   if (st != MLA_OK) return st;
   // full 128-row groups: q_lat goes to the workspace in the attention
   // kernel's operand order (each wave then loads one contiguous KiB per
   // k-step instead of 32 row pieces)
-  if (dt == MLA_BF16 && (S_q * n_h) % 128 == 0) {
-    p.q_swz = 1;
+  if (p.q_swz) {
     st = from_hip(launch_absorb_q_swizzled(q_nope, wkv_b, q_lat, BS, n_h, S_q, stream),
                   "absorb launch");
   } else {

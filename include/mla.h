@@ -193,6 +193,33 @@ mla_status mla_decode_latent_attn_multi(const void* q_lat, const void* q_pe, con
                                         hipStream_t stream);
 
 /*
+ * Packed queries: q_lat in the attention kernel's operand order, which lets
+ * each wave load the queries of one k-step as one contiguous KiB (with the
+ * row layout every 64-lane query load touches 32 separate rows). bf16 only,
+ * for S_q * n_h a multiple of 128. With R = S_q * n_h query rows per
+ * sequence (row v = j * n_h + h for token j, head h) and G = R / 128, the
+ * 16-byte slot
+ *   ((((b * G + v / 128) * 4 + (v / 32) % 4) * 32 + k) * 64 + 32 * e + v % 32)
+ * holds latent features 16k + 8e .. 16k + 8e + 7 of row v of sequence b
+ * (k < 32, e < 2): the same B * R * 512 elements as the row layout.
+ *   mla_absorb_q_packed: as mla_absorb_q for q_nope [B, S_q, n_h, 128],
+ *     writing q_packed ([KVR] first absorb identity; [ABS] excerpt).
+ *   mla_decode_latent_attn_packed: as mla_decode_latent_attn_multi with
+ *     q_lat given packed (same workspace size).
+ * Other dtypes or shapes return MLA_ERR_UNSUPPORTED.
+ */
+mla_status mla_absorb_q_packed(const void* q_nope, const void* wkv_b, void* q_packed, int B,
+                               int S_q, int n_h, mla_dtype dt, hipStream_t stream);
+mla_status mla_decode_latent_attn_packed(const void* q_packed, const void* q_pe,
+                                         const void* latent, const void* rope,
+                                         int64_t lat_bstride, int64_t lat_rstride,
+                                         int64_t rope_bstride, int64_t rope_rstride, int B,
+                                         int S_q, int n_h, int T, const int32_t* topk_idx, int K,
+                                         int causal, float scale, int num_splits, void* out_lat,
+                                         float* lse, void* workspace, size_t ws_bytes,
+                                         mla_dtype dt, hipStream_t stream);
+
+/*
  * The whole absorbed decode step in one call ([ABS] excerpt: absorb W^UK,
  * latent attention, W^UV): enqueues mla_absorb_q on B*S_q rows,
  * mla_decode_latent_attn_multi and mla_out_up on B*S_q rows, with q_lat and

@@ -156,6 +156,21 @@ def test_multi_token_argument_errors(lib):
     assert need >= 2 * (2 * 2 * 128 * 512 * 2) + binding.mla_decode_workspace_bytes(2, 256, 4096)
 
 
+def test_packed_query_argument_errors(lib):
+    # packed queries exist for bf16 and whole 128-row groups only
+    assert lib.mla_absorb_q_packed(FAKE, FAKE, FAKE, 2, 1, 64, BF16, None) == UNSUPPORTED
+    assert lib.mla_absorb_q_packed(FAKE, FAKE, FAKE, 2, 2, 64, F32, None) == UNSUPPORTED
+    assert lib.mla_absorb_q_packed(None, FAKE, FAKE, 2, 2, 64, BF16, None) == INVALID
+    assert lib.mla_absorb_q_packed(FAKE, FAKE, FAKE, 2, 0, 64, BF16, None) == INVALID
+    assert lib.mla_absorb_q_packed(None, None, None, 0, 1, 128, BF16, None) == OK
+    attn = lib.mla_decode_latent_attn_packed
+    args = [FAKE, FAKE, FAKE, FAKE, 4096 * 576, 576, 4096 * 576, 576, 2, 1, 64, 4096, None, 0,
+            0, 0.07, 0, FAKE, None, FAKE, 1 << 30, BF16, None]
+    assert attn(*args) == UNSUPPORTED                   # 64 rows: not a whole group
+    ok = list(args); ok[10] = 128; ok[0] = None
+    assert attn(*ok) == INVALID
+
+
 def append(lib, **kw):
     a = dict(kv=FAKE, rs=576, gamma=FAKE, eps=1e-6, freqs=FAKE, n_pos=4096, seq=None, pos=FAKE,
              N=8, lat=FAKE, rope=FAKE, lbs=4096 * 576, lrs=576, rbs=4096 * 576, rrs=576,

@@ -174,3 +174,35 @@ def test_decode_step_fused_merge_matches_the_separate_kernels(B, S_q, n_h, T):
     torch.cuda.synchronize()
     assert torch.equal(one.cpu().view(torch.int16), three.cpu().view(torch.int16))
     assert torch.equal(lse1.cpu(), lse3.cpu())
+
+
+def unpack_queries(packed, B, S_q, n_h):
+    """Row layout [B, S_q, n_h, 512] of packed queries, by the slot formula
+    the header states (plain numpy indexing)."""
+    R = S_q * n_h
+    G = R // 128
+    p = packed.reshape(B, G, 4, 32, 2, 32, 8)  # b, group, quarter, k-step, half, row%32, 8 features
+    rows = p.transpose(0, 1, 2, 5, 3, 4, 6).reshape(B, R, 512)
+    return rows.reshape(B, S_q, n_h, 512)
+
+
+@pytest.mark.parametrize("B,S_q,n_h", [(3, 1, 128), (2, 2, 64), (33, 1, 256)])
+def test_packed_queries_layout_and_attention(B, S_q, n_h):
+    T = 300
+    inp = multi_inputs(B, S_q, n_h, T, torch.bfloat16, seed=B + S_q + n_h)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    cache = d["cache"]
+    rows = mla.mla_absorb_q(d["q_nope"].reshape(B * S_q, n_h, 128), d["wkv_b"])
+    packed = mla.mla_absorb_q_packed(d["q_nope"], d["wkv_b"])
+    torch.cuda.synchronize()
+    un = unpack_queries(packed.cpu().view(torch.int16).numpy(), B, S_q, n_h)
+    assert np.array_equal(un, rows.cpu().view(torch.int16).numpy().reshape(B, S_q, n_h, 512))
+    causal = S_q > 1
+    a, la = mla.mla_decode_latent_attn_packed(packed, d["q_pe"], cache[..., :512],
+                                              cache[..., 512:], causal=causal, want_lse=True)
+    b, lb = mla.mla_decode_latent_attn_multi(rows.reshape(B, S_q, n_h, 512), d["q_pe"],
+                                             cache[..., :512], cache[..., 512:], causal=causal,
+                                             want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu().view(torch.int16), b.cpu().view(torch.int16))
+    assert torch.equal(la.cpu(), lb.cpu())
