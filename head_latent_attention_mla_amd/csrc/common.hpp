@@ -33,10 +33,14 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Two floats -> packed pair of bf16 (low half = a).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed pair of bf16 (low half = a), round to nearest-even:
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(float_to_bf16_bits(a)) |
-         (static_cast<uint32_t>(float_to_bf16_bits(b)) << 16);
+  const bf16x2 h = __builtin_convertvector(floatx2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
