@@ -235,57 +235,66 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
     if (!wave_live || t0 >= wkend) continue;  // nothing of this tile is visible to the wave
     const char* stage = at_lds + (it % AT_NSTAGE) * AT_STAGE;
 
+    // scores of both 32-key halves as two independent MFMA chains (a half
+    // wholly past the wave's keys is computed and masked to weight 0)
+    floatx16 s[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+    for (int ks = 0; ks < 12; ks++) {
+#pragma unroll
+      for (int half = 0; half < 2; half++) {
+        const bf16x8 A = as_bf16x8(
+            ld_lds16(stage + 32 * half * AT_K_PITCH + k_off[ks & 3] + 128 * (ks >> 2)));
+        s[half] = mfma32x32x16(A, as_bf16x8(qv[ks]), s[half]);
+      }
+    }
+    // mask: keys past T, past the query's position (causal), or outside the
+    // query's index set; one running-max update per 64-key tile
+    float tmax = -INFINITY;
 #pragma unroll
     for (int half = 0; half < 2; half++) {
-      const int tb = t0 + 32 * half;  // first key of the half-tile
-      if (tb >= wkend) break;
-      const char* kst = stage + 32 * half * AT_K_PITCH;
-      floatx16 s = floatx16{};
-#pragma unroll
-      for (int ks = 0; ks < 12; ks++) {
-        const bf16x8 A = as_bf16x8(ld_lds16(kst + k_off[ks & 3] + 128 * (ks >> 2)));
-        s = mfma32x32x16(A, as_bf16x8(qv[ks]), s);
-      }
-      // mask: keys past T, past the query's position (causal), or outside
-      // the query's index set
       uint32_t bits = 0xFFFFu;
       if (SPARSE) {
         const uint32_t* ms =
             reinterpret_cast<const uint32_t*>(stage + AT_K_BYTES + AT_V_BYTES) + half * AT_QBLOCK;
         bits = (ms[32 * wave + n] >> (16 * g)) & 0xFFFFu;
       }
-      float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int t = tb + 16 * g + r;
+        const int t = t0 + 32 * half + 16 * g + r;
         bool vis = t < p.T;
         if (CAUSAL) vis = vis && t <= qpos;
         if (SPARSE) vis = vis && ((bits >> r) & 1u);
-        s[r] = vis ? s[r] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, s[r]);
+        s[half][r] = vis ? s[half][r] * sl2 : -INFINITY;
+        tmax = fmaxf(tmax, s[half][r]);
       }
-      tmax = half_max(tmax);
-      const float m_new = fmaxf(m, tmax);
-      // a query that has seen no visible key yet keeps m = -inf: factor 1,
-      // weights exp2(-inf) = 0
-      const float f = m_new != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-      const float nm = m_new != -INFINITY ? -m_new : 0.f;
-      m = m_new;
-      l *= f;
+    }
+    tmax = half_max(tmax);
+    const float m_new = fmaxf(m, tmax);
+    // a query that has seen no visible key yet keeps m = -inf: factor 1,
+    // weights exp2(-inf) = 0
+    const float f = m_new != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+    const float nm = m_new != -INFINITY ? -m_new : 0.f;
+    m = m_new;
+    l *= f;
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) o[mt] *= f;
-      u32x4 P[2];
+    for (int mt = 0; mt < 4; mt++) o[mt] *= f;
+    u32x4 P[2][2];
+#pragma unroll
+    for (int half = 0; half < 2; half++)
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
 #pragma unroll
         for (int w2 = 0; w2 < 4; w2++) {
-          const float p0 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * w2] + nm);
-          const float p1 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * w2 + 1] + nm);
-          P[kk][w2] = pack_bf16x2(p0, p1);
+          const float p0 = __builtin_amdgcn_exp2f(s[half][8 * kk + 2 * w2] + nm);
+          const float p1 = __builtin_amdgcn_exp2f(s[half][8 * kk + 2 * w2 + 1] + nm);
+          P[half][kk][w2] = pack_bf16x2(p0, p1);
           // the denominator sums the rounded weights the mix uses
-          l += __uint_as_float(P[kk][w2] << 16) + __uint_as_float(P[kk][w2] & 0xFFFF0000u);
+          l += __uint_as_float(P[half][kk][w2] << 16) +
+               __uint_as_float(P[half][kk][w2] & 0xFFFF0000u);
         }
       }
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
       const char* vst = stage + AT_K_BYTES + 32 * half * AT_V_PITCH;
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
         for (int kk = 0; kk < 2; kk++) {
           const char* lo = vst + v_off[mt] + 8 * kk * AT_V_PITCH;
           const bf16x8 A = at_tr_pair(lo, lo + 4 * AT_V_PITCH);
-          o[mt] = mfma32x32x16(A, as_bf16x8(P[kk]), o[mt]);
+          o[mt] = mfma32x32x16(A, as_bf16x8(P[half][kk]), o[mt]);
         }
       }
     }
