@@ -35,8 +35,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dtype_ok(mla_dtype dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
 // Split plan of the decode call: rows are cut into 32-row tiles, splits get
-// equal tile counts. Automatic choice: aim at one 4-wave workgroup per
-// compute unit (256 on MI355X) without making any split empty.
+// equal tile counts. Automatic choice: aim at one workgroup (8 waves, nearly
+// all of the LDS) per compute unit (256 on MI355X) without making any split
+// empty.
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxSplits = 1024;
 // The top-k kernel stages one split's indices in LDS: at most 1024 rows.
