@@ -18,7 +18,10 @@
 //       A = key rows read from LDS in the row order pi, so accumulator r of
 //       lane half g is key 16g + r; B = the wave's queries, in registers)
 //   online softmax in the log2 domain, per lane (each lane holds one query
-//       and 16 keys; one cross-half exchange per max)
+//       and 16 keys; one cross-half exchange per max); the running max is
+//       raised lazily (only when a score beats it by 2^8), so the output
+//       accumulators are rescaled rarely, and tiles wholly visible to the
+//       wave skip the mask
 //   O^T[128 x 32] += V^T . P^T   (8 MFMAs; A = value rows read with the
 //       gfx950 transposing LDS load ds_read_b64_tr_b16; B = P straight from
 //       the score accumulators)
@@ -64,6 +67,7 @@ constexpr int AT_V_DMA = AT_V_BYTES / 1024 / AT_WAVES;  // 2
 constexpr int AT_DMA = AT_K_DMA + AT_V_DMA;        // + 1 mask DMA on waves 0, 1 (index sets)
 constexpr float AT_LOG2E = 1.4426950408889634f;
 constexpr float AT_LN2 = 0.6931471805599453f;
+constexpr float AT_SLACK = 8.0f;  // log2 units by which a score may exceed the running max
 
 static_assert(AT_K_BYTES % (1024 * AT_WAVES) == 0 && AT_V_BYTES % (1024 * AT_WAVES) == 0,
               "tiles must split into whole wave-DMAs");
@@ -248,36 +252,51 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
       }
     }
     // mask: keys past T, past the query's position (causal), or outside the
-    // query's index set; one running-max update per 64-key tile
-    float tmax = -INFINITY;
+    // query's index set. A tile wholly visible to the wave (all dense tiles
+    // but the last and the causal diagonal) needs no mask.
+    const bool all_visible =
+        !SPARSE && t0 + AT_KT <= p.T && (!CAUSAL || t0 + AT_KT - 1 <= shift + qw);
+    if (!all_visible) {
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
-      uint32_t bits = 0xFFFFu;
-      if (SPARSE) {
-        const uint32_t* ms =
-            reinterpret_cast<const uint32_t*>(stage + AT_K_BYTES + AT_V_BYTES) + half * AT_QBLOCK;
-        bits = (ms[32 * wave + n] >> (16 * g)) & 0xFFFFu;
-      }
+      for (int half = 0; half < 2; half++) {
+        uint32_t bits = 0xFFFFu;
+        if (SPARSE) {
+          const uint32_t* ms =
+              reinterpret_cast<const uint32_t*>(stage + AT_K_BYTES + AT_V_BYTES) + half * AT_QBLOCK;
+          bits = (ms[32 * wave + n] >> (16 * g)) & 0xFFFFu;
+        }
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int t = t0 + 32 * half + 16 * g + r;
-        bool vis = t < p.T;
-        if (CAUSAL) vis = vis && t <= qpos;
-        if (SPARSE) vis = vis && ((bits >> r) & 1u);
-        s[half][r] = vis ? s[half][r] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, s[half][r]);
+        for (int r = 0; r < 16; r++) {
+          const int t = t0 + 32 * half + 16 * g + r;
+          bool vis = t < p.T;
+          if (CAUSAL) vis = vis && t <= qpos;
+          if (SPARSE) vis = vis && ((bits >> r) & 1u);
+          s[half][r] = vis ? s[half][r] : -INFINITY;
+        }
       }
     }
-    tmax = half_max(tmax);
-    const float m_new = fmaxf(m, tmax);
+    // one running-max update per 64-key tile, in the log2 domain; the scale
+    // is positive, so the max of the scaled scores is the scaled max. The max
+    // is raised lazily (only when a score beats it by 2^8), so the output
+    // accumulators are rescaled only then; weights stay below 2^8.
+    float smax = -INFINITY;
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) smax = fmaxf(smax, s[half][r]);
+    const float tmax = half_max(smax) * sl2;
+    const bool rescaled = __any(tmax > m + AT_SLACK);
+    const float m_new = rescaled ? fmaxf(m, tmax) : m;
     // a query that has seen no visible key yet keeps m = -inf: factor 1,
     // weights exp2(-inf) = 0
-    const float f = m_new != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-    const float nm = m_new != -INFINITY ? -m_new : 0.f;
-    m = m_new;
-    l *= f;
+    if (rescaled) {
+      const float f = m_new != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+      l *= f;
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++) o[mt] *= f;
+      for (int mt = 0; mt < 4; mt++) o[mt] *= f;
+    }
+    m = m_new;
+    const float nm = m != -INFINITY ? -m : 0.f;
     u32x4 P[2][2];
 #pragma unroll
     for (int half = 0; half < 2; half++)
@@ -285,8 +304,8 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
       for (int kk = 0; kk < 2; kk++) {
 #pragma unroll
         for (int w2 = 0; w2 < 4; w2++) {
-          const float p0 = __builtin_amdgcn_exp2f(s[half][8 * kk + 2 * w2] + nm);
-          const float p1 = __builtin_amdgcn_exp2f(s[half][8 * kk + 2 * w2 + 1] + nm);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[half][8 * kk + 2 * w2], sl2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[half][8 * kk + 2 * w2 + 1], sl2, nm));
           P[half][kk][w2] = pack_bf16x2(p0, p1);
           // the denominator sums the rounded weights the mix uses
           l += __uint_as_float(P[half][kk][w2] << 16) +
