@@ -237,6 +237,8 @@ def test_decode_empty_batch_is_noop():
 
 @pytest.mark.parametrize("N,n_h,dtype", [(1, 16, torch.bfloat16), (100, 16, torch.bfloat16),
                                          (300, 128, torch.bfloat16), (257, 48, torch.bfloat16),
+                                         # several tiles per workgroup, with ragged tails
+                                         (600, 128, torch.bfloat16), (1000, 200, torch.bfloat16),
                                          (37, 16, torch.float32), (5, 128, torch.float32)])
 def test_kv_reconstruct(N, n_h, dtype):
     inp = synth.reconstruct_inputs(N, n_h, dtype, seed=N + n_h)
