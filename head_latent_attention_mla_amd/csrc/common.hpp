@@ -70,15 +70,22 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
 // One wave-wide 16-byte-per-lane load from global memory straight into LDS:
 // lane i's 16 bytes at (rsrc base + soff + voff) land at LDS byte
 // lds_dst + 16*i. Issued from inline assembly so the compiler does not
-// serialise consecutive LDS-DMA loads; it has no register outputs, and the
-// caller waits with an explicit s_waitcnt vmcnt before the barrier that
+// serialise consecutive LDS-DMA loads; it has no register outputs (m0, which
+// it overwrites, is declared clobbered), and the caller waits with an explicit s_waitcnt vmcnt before the barrier that
 // publishes the data.
+// The compiler keeps m0 reserved and sets it right before each of its own
+// uses, so nothing needs to survive across this statement; the clobber only
+// orders the statement against those uses (clang's note that a reserved
+// register is not preserved across the statement is what is wanted here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {

@@ -229,6 +229,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   __shared__ __attribute__((aligned(16))) int flag[4];             // head quarter rescaled
   __shared__ float linv[128];                                      // 1 / sum per head
   __shared__ int idx_lds[SPARSE ? MAX_SPARSE_ROWS : 1];
+  // bit r of word k: row 32k + r of this split is a position of the index set
+  __shared__ uint32_t vmask[SPARSE ? MAX_SPARSE_ROWS / 32 : 1];
 
   // Workgroups are dealt to the 8 XCDs round-robin in launch order. Renumber
   // them so that the splits of one (sequence, head group) run on one XCD and
@@ -267,8 +269,23 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const uint32_t tiles_addr = __builtin_amdgcn_readfirstlane(lds_addr(tiles));
 
   if (SPARSE) {
+    // The index set is a scatter into a -inf row: an entry outside [0, T)
+    // addresses no position. Such entries are staged as row 0 (so every
+    // fetch stays inside the cache) and cleared in vmask (weight zero).
     const int* src = p.idx + static_cast<int64_t>(b) * p.K + row_begin;
-    for (int i = threadIdx.x; i < row_end - row_begin; i += NWAVES * 64) idx_lds[i] = src[i];
+    const int n_rows = row_end - row_begin;
+    for (int i0 = 0; i0 < n_rows; i0 += NWAVES * 64) {
+      const int i = i0 + threadIdx.x;
+      const int v = i < n_rows ? src[i] : -1;
+      const bool ok = v >= 0 && v < p.T;
+      if (i < n_rows) idx_lds[i] = ok ? v : 0;
+      const uint64_t bal = __ballot(ok);
+      // i is a multiple of 64 on lane 0: words i/32 and i/32 + 1
+      if (lane == 0 && i < MAX_SPARSE_ROWS) {
+        vmask[i >> 5] = static_cast<uint32_t>(bal);
+        vmask[(i >> 5) + 1] = static_cast<uint32_t>(bal >> 32);
+      }
+    }
     __syncthreads();
   }
   // prologue DMA of tile 0; the query loads that follow are waited for
@@ -484,9 +501,17 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       // partial scores of tile it+1 (on the last tile they read a stale
       // buffer and are discarded); the partner's multiplies fill the
       // SIMD's MFMA pipe meanwhile ----
-      const int valid = row_vis - (row_begin + it * TILE);  // visible rows of this tile
+      if (SPARSE) {
+        // rows of this lane: tile rows 16g..16g+15 (rows past the split are
+        // clear in vmask too)
+        const uint32_t bits = vmask[it] >> (16 * g);
 #pragma unroll
-      for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
+        for (int r = 0; r < 16; r++) S[r] = (bits >> r) & 1u ? S[r] : -INFINITY;
+      } else {
+        const int valid = row_vis - (row_begin + it * TILE);  // visible rows of this tile
+#pragma unroll
+        for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
+      }
       float smax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r++) smax = fmaxf(smax, S[r]);
@@ -495,12 +520,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       const bool rescaled = __any(tmax > m + RESCALE_SLACK);
       const float m_new = rescaled ? fmaxf(m, tmax) : m;
       // 0 on the first tile; a head that has seen no visible row yet (causal
-      // limit) keeps m = -inf, factor 1 and weights exp2(-inf) = 0
-      const float f = rescaled && (!CAUSAL || m_new != -INFINITY)
+      // limit, or index entries outside [0, T)) keeps m = -inf, factor 1 and
+      // weights exp2(-inf) = 0
+      constexpr bool MAYBE_EMPTY = CAUSAL || SPARSE;
+      const float f = rescaled && (!MAYBE_EMPTY || m_new != -INFINITY)
                           ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
       l *= f;
       m = m_new;
-      const float nm = !CAUSAL || m != -INFINITY ? -m : 0.f;
+      const float nm = !MAYBE_EMPTY || m != -INFINITY ? -m : 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 P;
@@ -561,7 +588,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   if (kh == 1 && active) {
     const float l_tot = pair_sum(l);
     // a head with no visible row in this split: zero partial, lse -inf
-    if (g == 0) linv[hq * 32 + n] = !CAUSAL || l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (g == 0) linv[hq * 32 + n] = !(CAUSAL || SPARSE) || l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (g == 0 && head < p.n_h) {
       const float lse_v = (m + log2f(l_tot)) * LN2;  // natural log of sum exp(z)
       const int64_t bh = static_cast<int64_t>(b) * p.n_h + head;
@@ -624,13 +651,14 @@ __global__ __launch_bounds__(64) void merge_splits_f32_kernel(const T* __restric
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int c0 = threadIdx.x * 8;
   for (int s = 0; s < S; s++) {
-    const float w = __expf(ws_lse[s * BH + bh] - mx);
+    // no split saw a position (every index outside [0, T)): the empty sum
+    const float w = mx != -INFINITY ? __expf(ws_lse[s * BH + bh] - mx) : 0.f;
     wsum += w;
     const T* src = ws_o + (s * BH + bh) * D_C + c0;
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = fmaf(w, ld_elem<T>(src, i), acc[i]);
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; i++) st_elem(out, bh * D_C + c0 + i, acc[i] * inv);
   if (threadIdx.x == 0 && lse) lse[bh] = mx + logf(wsum);
@@ -682,8 +710,17 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
     const int rr = r0 + tid;
     float t = -INFINITY;
     int tok = 0;
-    if (rr < row_end) {
-      tok = p.idx ? p.idx[static_cast<int64_t>(b) * p.K + rr] : rr;
+    // an index entry outside [0, T) addresses no position: weight zero,
+    // and row 0 stands in for it in the mix
+    bool live = rr < row_end;
+    if (live && p.idx) {
+      tok = p.idx[static_cast<int64_t>(b) * p.K + rr];
+      live = tok >= 0 && tok < p.T;
+      if (!live) tok = 0;
+    } else if (live) {
+      tok = rr;
+    }
+    if (live) {
       const float* lrow = lat + static_cast<int64_t>(tok) * p.lat_rs;
       const float* rrow = rp + static_cast<int64_t>(tok) * p.rope_rs;
       float content = 0.f, rotary = 0.f;
@@ -700,7 +737,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
     __syncthreads();
     const float m_new = fmaxf(m, tmax);
     const float f = m_new != -INFINITY ? expf(m - m_new) : 1.f;
-    const float pv = rr < row_end ? expf(t - m_new) : 0.f;
+    const float pv = live ? expf(t - m_new) : 0.f;
     ps[tid] = pv;
     ts[tid] = tok;
     float sv = pv;

@@ -17,7 +17,8 @@ constexpr int MERGE_CHUNK = 8;  // splits per memory round trip
 // are loaded together (one memory round trip per chunk; indices past the
 // last split are clamped and weighted zero) and folded in with a running
 // maximum. Returns the merged values (fp32, before rounding) and each row's
-// log-sum-exp. The arithmetic of a row does not depend on NR.
+// log-sum-exp; a row whose splits all saw no position (lse -inf) merges to
+// zero with lse -inf. The arithmetic of a row does not depend on NR.
 template <int NR>
 __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
                                             const float* __restrict__ ws_lse, int S, int64_t BH,
@@ -47,14 +48,16 @@ __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
       float cm = mx[r];
 #pragma unroll
       for (int j = 0; j < MERGE_CHUNK; j++) cm = fmaxf(cm, lv[r][j]);
-      const float f = __expf(mx[r] - cm);  // 0 on the first chunk (mx = -inf)
+      // f is 0 on the first chunk (mx = -inf); while no split has seen a
+      // position (cm = -inf: every index outside [0, T)) nothing is added
+      const float f = cm != -INFINITY ? __expf(mx[r] - cm) : 1.f;
       wsum[r] *= f;
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[r][i] *= f;
       mx[r] = cm;
 #pragma unroll
       for (int j = 0; j < MERGE_CHUNK; j++) {
-        const float w = s0 + j < S ? __expf(lv[r][j] - mx[r]) : 0.f;
+        const float w = s0 + j < S && cm != -INFINITY ? __expf(lv[r][j] - mx[r]) : 0.f;
         wsum[r] += w;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -66,7 +69,7 @@ __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
   }
 #pragma unroll
   for (int r = 0; r < NR; r++) {
-    const float inv = 1.f / wsum[r];
+    const float inv = wsum[r] > 0.f ? 1.f / wsum[r] : 0.f;  // the empty sum is 0
 #pragma unroll
     for (int i = 0; i < 8; i++) out[r][i] = acc[r][i] * inv;
     lse[r] = mx[r] + logf(wsum[r]);

@@ -130,10 +130,16 @@ int mla_decode_num_splits(int B, int n_h, int T, int K);
  *          [:B, :T], or one packed [B,T,576] cache with latent = p,
  *          rope = p + 512 and both row strides 576.
  *   topk_idx  NULL for dense attention over all T positions (K ignored), or
- *          int32 [B, K] with 1 <= K <= T DISTINCT positions in [0, T) per
- *          sequence, in any order. Index contents are NOT checked on the
- *          device: out-of-range entries read outside the cache and
- *          duplicates are counted twice; callers must guarantee the contract.
+ *          int32 [B, K], 1 <= K <= T, in any order: the positions the index
+ *          mask leaves visible ([ABS] excerpt: 0 scattered into a -inf row).
+ *          An entry outside [0, T) addresses no position and is ignored
+ *          (e.g. -1 padding; no memory outside the cache is read); a
+ *          sequence whose entries are all outside [0, T) gets the empty sum:
+ *          out_lat = 0 and lse = -inf. The in-range entries of a row must be
+ *          DISTINCT (as a top-k selection produces): each is gathered once,
+ *          so a repeated position would be counted once per repeat. The
+ *          naive path's mla_attention_naive, which stages the set as a bit
+ *          mask, also accepts repeats.
  *   out_lat [B, n_h, 512] (dt, out), lse [B, n_h] float32 (out, or NULL).
  *   num_splits  number of partitions of the attended positions (0 = let the
  *          library choose; otherwise lo <= num_splits <= ceil(rows/32), where

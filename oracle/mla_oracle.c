@@ -143,23 +143,26 @@ int orc_absorb_q(const void* q_nope, int dt_q, const void* w, int dt_w, int B,
 
 /* ---- index mask ------------------------------------------------------------ */
 
-/* Fills allowed[0..T) for one sequence: every position when idx is NULL,
- * otherwise exactly the K listed positions. The mask of the excerpt is a
- * scatter into a -inf row, i.e. a set; this oracle additionally rejects
- * out-of-range or repeated entries because the GPU contract requires
- * distinct in-range indices. */
+/* Fills allowed[0..T) for one sequence and returns how many positions are
+ * allowed: every position when idx is NULL, otherwise the set the index
+ * mask of the excerpts marks. Both excerpts build that mask by scattering 0
+ * into a row of -inf at the listed positions, so the listed entries form a
+ * set: a repeated entry marks its position once, and an entry outside
+ * [0, T) addresses no position and marks nothing. */
 static int build_allowed(const int32_t* idx, int K, int T, unsigned char* allowed) {
   if (!idx) {
     memset(allowed, 1, (size_t)T);
-    return 0;
+    return T;
   }
   memset(allowed, 0, (size_t)T);
+  int n = 0;
   for (int k = 0; k < K; k++) {
     int32_t t = idx[k];
-    if (t < 0 || t >= T || allowed[t]) return -1;
+    if (t < 0 || t >= T || allowed[t]) continue;
     allowed[t] = 1;
+    n++;
   }
-  return 0;
+  return n;
 }
 
 /* softmax over the allowed positions of z[0..T) (disallowed entries are -inf
@@ -187,7 +190,10 @@ static double softmax_inplace(double* z, const unsigned char* allowed, int T) {
  * Latent element (b,t,c) is at latent[b*lat_bs + t*lat_rs + c], rotary
  * element (b,t,r) at rope[b*rope_bs + t*rope_rs + r].
  * Optional outputs: lse[b,h] = log sum_t exp z[t]; probs[b,h,t] = p[t].
- * Parity: pinned (naive-path identity, closed forms, permutation). */
+ * A sequence whose index set marks no position gets the empty sum: zero
+ * output, lse = -inf, zero probabilities.
+ * Parity: pinned (naive-path identity, closed forms, permutation, torch
+ * SDPA with the set's boolean mask). */
 int orc_latent_attention(const void* q_lat, int dt_ql, const void* q_pe, int dt_qp,
                          const void* latent, const void* rope, int dt_cache,
                          int64_t lat_bs, int64_t lat_rs, int64_t rope_bs,
@@ -197,24 +203,33 @@ int orc_latent_attention(const void* q_lat, int dt_ql, const void* q_pe, int dt_
   if (B < 0 || n_h < 1 || T < 1 || d_c < 1 || d_r < 0) return -1;
   if (idx && (K < 1 || K > T)) return -1;
   unsigned char* allowed = (unsigned char*)malloc((size_t)B * T);
-  if (!allowed) return -2;
+  int* nallowed = (int*)malloc(sizeof(int) * (size_t)(B ? B : 1));
+  if (!allowed || !nallowed) {
+    free(allowed);
+    free(nallowed);
+    return -2;
+  }
   for (int b = 0; b < B; b++)
-    if (build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, allowed + (int64_t)b * T)) {
-      free(allowed);
-      return -1;
-    }
+    nallowed[b] = build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, allowed + (int64_t)b * T);
   int bad = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; b++)
     for (int h = 0; h < n_h; h++) {
       const unsigned char* al = allowed + (int64_t)b * T;
+      int64_t qrow = (int64_t)b * n_h + h;
+      if (nallowed[b] == 0) { /* no position in the set: empty sum, zero output */
+        for (int c = 0; c < d_c; c++) out_lat[qrow * d_c + c] = 0.0;
+        if (lse) lse[qrow] = -INFINITY;
+        if (probs)
+          for (int t = 0; t < T; t++) probs[qrow * T + t] = 0.0;
+        continue;
+      }
       double* z = (double*)malloc(sizeof(double) * (size_t)T);
       if (!z) {
 #pragma omp atomic write
         bad = 1;
         continue;
       }
-      int64_t qrow = (int64_t)b * n_h + h;
       for (int t = 0; t < T; t++) {
         if (!al[t]) {
           z[t] = -INFINITY;
@@ -243,6 +258,7 @@ int orc_latent_attention(const void* q_lat, int dt_ql, const void* q_pe, int dt_
       free(z);
     }
   free(allowed);
+  free(nallowed);
   return bad ? -2 : 0;
 }
 
@@ -274,10 +290,7 @@ int orc_latent_attention_multi(const void* q_lat, int dt_ql, const void* q_pe, i
   unsigned char* allowed = (unsigned char*)malloc((size_t)B * T);
   if (!allowed) return -2;
   for (int b = 0; b < B; b++)
-    if (build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, allowed + (int64_t)b * T)) {
-      free(allowed);
-      return -1;
-    }
+    build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, allowed + (int64_t)b * T);
   int bad = 0;
 #pragma omp parallel for collapse(3) schedule(dynamic)
   for (int b = 0; b < B; b++)
@@ -431,8 +444,10 @@ int orc_kv_reconstruct(const void* c, const void* k_rope, int dt_in, const void*
  *   z[t] = scale * <[q_nope ; q_pe], K[t,h]>,  -inf outside the index set,
  *   p = softmax(z),  out[b,h] = sum_t p[t] V[t,h]
  * ("Value up-projection" prefill excerpt, restricted to the last query row,
- * which sees every cached position). out [B,n_h,d_v], probs optional.
- * Parity: pinned (torch scaled_dot_product_attention in double). */
+ * which sees every cached position). out [B,n_h,d_v], probs optional; a
+ * sequence whose index set marks no position gets a zero output.
+ * Parity: pinned (torch scaled_dot_product_attention in double, incl. index
+ * sets with repeats and out-of-range entries). */
 int orc_decode_naive(const void* q_nope, const void* q_pe, int dt_q, const void* latent,
                      const void* rope, int dt_cache, int64_t lat_bs, int64_t lat_rs,
                      int64_t rope_bs, int64_t rope_rs, const void* w, int dt_w, int B,
@@ -449,9 +464,15 @@ int orc_decode_naive(const void* q_nope, const void* q_pe, int dt_q, const void*
   unsigned char* al = (unsigned char*)malloc((size_t)T);
   int rc = (Kb && Vb && z && al) ? 0 : -2;
   for (int b = 0; b < B && !rc; b++) {
-    if (build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, al)) {
-      rc = -1;
-      break;
+    if (build_allowed(idx ? idx + (int64_t)b * K : NULL, K, T, al) == 0) {
+      /* no position in the set: empty sum, zero output */
+      for (int h = 0; h < n_h; h++) {
+        int64_t qrow = (int64_t)b * n_h + h;
+        for (int d = 0; d < d_v; d++) out[qrow * d_v + d] = 0.0;
+        if (probs)
+          for (int t = 0; t < T; t++) probs[qrow * T + t] = 0.0;
+      }
+      continue;
     }
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
@@ -591,14 +612,14 @@ int orc_attention_naive(const void* q, const void* k, const void* v, int dt, int
       for (int h = 0; h < n_h; h++) {
         unsigned char* al = (unsigned char*)malloc((size_t)T);
         double* z = (double*)malloc(sizeof(double) * (size_t)T);
-        if (!al || !z ||
-            build_allowed(idx ? idx + ((int64_t)b * S + s) * K : NULL, K, T, al)) {
+        if (!al || !z) {
 #pragma omp atomic write
           bad = 1;
           free(al);
           free(z);
           continue;
         }
+        build_allowed(idx ? idx + ((int64_t)b * S + s) * K : NULL, K, T, al);
         int any = 0;
         for (int t = 0; t < T; t++) {
           if (causal && t > T - S + s) al[t] = 0;

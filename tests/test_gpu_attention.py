@@ -88,6 +88,31 @@ def test_repeated_indices_count_once():
     assert torch.equal(a.cpu().view(torch.int16), b.cpu().view(torch.int16))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_index_sets_with_repeats_and_out_of_range_entries(causal, dtype):
+    # the mask is a scatter into a -inf row: repeats mark a position once and
+    # entries outside [0, T) mark nothing; the oracle follows the same set
+    # reading, independently of the GPU's bit mask
+    B, S, T, n_h, K = 2, 130, 190, 2, 40
+    inp = synth.attention_inputs(B, S, T, n_h, dtype, seed=11, topk=K - 12, causal=causal)
+    g = np.random.default_rng(12)
+    base = inp["topk_idx"].numpy()
+    bad = np.array([-1, T, T + 64, -(2 ** 31), 2 ** 31 - 1], np.int64)
+    idx = np.empty((B, S, K), np.int64)
+    for b in range(B):
+        for s in range(S):
+            row = np.concatenate([base[b, s], base[b, s, :6], bad[g.integers(5, size=6)]])
+            idx[b, s] = row[g.permutation(K)]
+    idx = torch.from_numpy(idx.astype(np.int32))
+    out, lse = mla.mla_attention_naive(inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV),
+                                       topk_idx=idx.to(DEV), causal=causal, want_lse=True)
+    ref, ref_lse = oracle.attention_naive(inp["q"], inp["k"], inp["v"], topk_idx=idx,
+                                          causal=causal)
+    check(out.cpu().double().numpy(), ref, TOL[dtype], "out")
+    check(lse.cpu().double().numpy(), ref_lse, TOL[dtype], "lse")
+
+
 def test_prefill_full_size_sampled_queries():
     # S = T = 8192 tokens, 128 heads, causal: the launch the benchmark times;
     # eight queries (all heads) against the oracle over their visible keys

@@ -223,6 +223,61 @@ def test_decode_full_topk_equals_dense():
     check(f64(sparse), f64(dense), BF16_TOL, "K=T sparse vs dense")
 
 
+def _with_invalid_entries(topk, T, seed, empty_rows=(), lead=0):
+    """Replace some entries of each index row by values outside [0, T) (-1
+    padding, T, far beyond, the int32 extremes); rows in empty_rows become
+    wholly invalid; with lead > 0 the first lead entries of every row are
+    invalid (a whole leading split sees no position)."""
+    g = np.random.default_rng(seed)
+    idx = topk.numpy().copy()
+    bad = np.array([-1, T, T + 1000, -(2 ** 31), 2 ** 31 - 1], np.int64)
+    B, K = idx.shape
+    for b in range(B):
+        where = g.choice(K, K // 7, replace=False)
+        idx[b, where] = bad[g.integers(len(bad), size=len(where))]
+        if lead:
+            idx[b, :lead] = bad[g.integers(len(bad), size=lead)]
+        if b in empty_rows:
+            idx[b] = bad[g.integers(len(bad), size=K)]
+    return torch.from_numpy(idx.astype(np.int32))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("splits", [0, 1, 4])
+def test_decode_index_entries_outside_the_cache_are_ignored(dtype, splits):
+    # the mask is a scatter into a -inf row: an entry outside [0, T) marks no
+    # position (padding such as -1). Sequence 2's set marks nothing at all:
+    # the empty sum, zero output and lse -inf. The first 64 entries of every
+    # row are invalid, so with 4 splits a whole split sees no position.
+    B, n_h, T, K = 3, 128, 700, 300
+    inp = synth.decode_inputs(B, n_h, T, dtype, seed=91, topk=K, stage_inputs=True)
+    topk = _with_invalid_entries(inp["topk_idx"], T, seed=92, empty_rows=(2,), lead=64)
+    out, lse = run_decode(inp, topk=topk, num_splits=splits)
+    ref_o, ref_lse = oracle_decode(inp, topk=topk)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    o, l = f64(out), host(lse).double().numpy()
+    check(o[:2], ref_o[:2], tol, "out_lat")
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(l[2])) and np.all(np.isneginf(ref_lse[2]))
+    assert np.max(np.abs(l[:2] - ref_lse[:2])) <= (2.0 ** -8 if dtype == torch.bfloat16 else 1e-5)
+
+
+def test_decode_step_index_entries_outside_the_cache_are_ignored():
+    # the one-call step (split merge fused into W^UV) on the same kind of set
+    B, n_h, T, K = 3, 128, 2000, 1500
+    inp = synth.decode_inputs(B, n_h, T, torch.bfloat16, seed=93, topk=K)
+    topk = _with_invalid_entries(inp["topk_idx"], T, seed=94, empty_rows=(1,), lead=200)
+    cache = cuda(inp["cache"])
+    out, lse = mla.mla_decode_step(cuda(inp["q_nope"]), cuda(inp["q_pe"]), cuda(inp["wkv_b"]),
+                                   cache[..., :512], cache[..., 512:], topk_idx=cuda(topk),
+                                   want_lse=True)
+    c = inp["cache"]
+    ref = oracle.decode_absorbed(inp["q_nope"], inp["q_pe"], c[..., :512], c[..., 512:],
+                                 inp["wkv_b"], topk_idx=topk, want_lse=True)
+    o = f64(out)
+    check(o[[0, 2]], ref["out"][[0, 2]], BF16_TOL, "out")
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(host(lse).double().numpy()[1]))
+
+
 def test_decode_empty_batch_is_noop():
     q = torch.empty((0, 128, 512), dtype=torch.bfloat16, device=DEV)
     qp = torch.empty((0, 128, 64), dtype=torch.bfloat16, device=DEV)
@@ -286,6 +341,18 @@ def test_config1_tiny_fp32_both_paths():
     Kr, Vr = oracle.kv_reconstruct(cache[0, :, :512], cache[0, :, 512:], w, 16)
     check(f64(K), Kr, F32_TOL, "K")
     check(f64(V), Vr, F32_TOL, "V")
+    # ... and the naive path's attention over them on the GPU: the one query
+    # q = [q_nope ; q_pe] sits at the end of the 128 cached positions and sees
+    # them all; scale 1/sqrt(192). The whole naive chain on the GPU equals the
+    # oracle's naive and absorbed paths and the GPU absorbed path.
+    T = cache.shape[1]
+    q = torch.cat([inp["q_nope"], inp["q_pe"]], -1)[:, None].contiguous()  # [1, 1, 16, 192]
+    naive = mla.mla_attention_naive(cuda(q), K.view(1, T, 16, 192), V.view(1, T, 16, 128),
+                                    causal=True, scale=192 ** -0.5)
+    got = f64(naive)[:, 0]
+    check(got, ref_naive, F32_TOL, "GPU naive chain vs oracle naive")
+    check(got, ref_abs, F32_TOL, "GPU naive chain vs oracle absorbed")
+    check(got, f64(out), F32_TOL, "GPU naive chain vs GPU absorbed")
 
 
 @pytest.mark.parametrize("cfg", [2, 3])

@@ -129,14 +129,40 @@ def test_naive_and_absorbed_differ_if_wuk_wuv_swapped():
 # naive path against torch's scaled dot-product attention (double, CPU)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("masked", [False, True])
+def _dirty_sets(g, rows, T, K, n_bad=4, n_rep=3):
+    """Index rows of K entries: distinct in-range positions, then repeats of
+    some of them and entries outside [0, T) (padding -1, T, beyond), in a
+    shuffled order."""
+    out = np.empty((rows, K), np.int32)
+    for r in range(rows):
+        good = g.choice(T, K - n_bad - n_rep, replace=False)
+        bad = np.array([-1, T, T + 7, -(2 ** 31)], np.int64)[:n_bad]
+        row = np.concatenate([good, good[:n_rep], bad]).astype(np.int32)
+        out[r] = row[g.permutation(K)]
+    return out
+
+
+def _set_mask(idx, T):
+    """Boolean [rows, T] mask of the in-range entries of each index row."""
+    flat = idx.reshape(-1, idx.shape[-1])
+    m = np.zeros((flat.shape[0], T), bool)
+    for r, row in enumerate(flat):
+        m[r, row[(row >= 0) & (row < T)]] = True
+    return m.reshape(idx.shape[:-1] + (T,))
+
+
+@pytest.mark.parametrize("masked", [False, True, "dirty"])
 def test_naive_matches_torch_sdpa(masked):
     B, n_h, T = 2, 4, 50
     p = tiny_problem(21, B, n_h, T, d_c=512, d_r=64, d_n=128, d_v=128)
     scale = 192 ** -0.5
     idx = None
     allowed = np.ones((B, T), bool)
-    if masked:
+    if masked == "dirty":
+        # repeats and out-of-range entries: the scatter marks a set
+        idx = _dirty_sets(rng(23), B, T, 24)
+        allowed = _set_mask(idx, T)
+    elif masked:
         g = rng(22)
         idx = np.stack([g.choice(T, 17, replace=False) for _ in range(B)]).astype(np.int32)
         allowed[:] = False
@@ -302,11 +328,25 @@ def test_permutation_invariance():
     assert rel_err(a3["out"], a["out"]) < 1e-13
 
 
-def test_bad_index_sets_are_rejected():
-    p = tiny_problem(52, 1, 1, 8)
-    for bad in ([[1, 1]], [[8]], [[-1]]):
-        with pytest.raises(ValueError):
-            run_both(p, topk_idx=np.array(bad, np.int32))
+def test_index_sets_are_sets():
+    # the mask is a scatter into a -inf row: repeats mark a position once,
+    # entries outside [0, T) mark nothing
+    p = tiny_problem(52, 2, 3, 8)
+    a, n = run_both(p, topk_idx=np.array([[1, 5, 1, -1], [8, 0, 0, 3]], np.int32))
+    c, _ = run_both(p, topk_idx=np.array([[1, 5], [0, 3]], np.int32))
+    assert rel_err(a["out"], c["out"]) < 1e-14 and rel_err(n["out"], c["out"]) < 1e-14
+    # a set that marks no position: the empty sum (zero output, lse -inf)
+    e = oracle.decode_absorbed(p["q_nope"], p["q_pe"], p["latent"], p["rope"], p["w"],
+                               topk_idx=np.array([[-1, 8], [1, 1]], np.int32), scale=0.3,
+                               d_n=p["d_n"], d_v=p["d_v"], want_lse=True, want_probs=True)
+    assert np.all(e["out"][0] == 0.0) and np.all(np.isneginf(e["lse"][0]))
+    assert np.all(e["probs"][0] == 0.0)
+    np.testing.assert_allclose(e["probs"][1, :, 1], 1.0, rtol=1e-15)
+    nn = oracle.decode_naive(p["q_nope"], p["q_pe"], p["latent"], p["rope"], p["w"],
+                             topk_idx=np.array([[-1, 8], [1, 1]], np.int32), scale=0.3,
+                             d_n=p["d_n"], d_v=p["d_v"])
+    assert np.all(nn["out"][0] == 0.0)
+    assert rel_err(nn["out"][1], e["out"][1]) < 1e-13
 
 
 def test_stage_functions_compose_to_the_whole_path():
@@ -627,13 +667,23 @@ def _naive_problem(seed, B, S, T, n_h, d_qk=12, d_v=5):
 
 
 @pytest.mark.parametrize("S,T,causal,K", [(7, 7, True, None), (5, 11, True, 4),
-                                          (6, 9, False, 3), (4, 4, False, None)])
+                                          (6, 9, False, 3), (4, 4, False, None),
+                                          (6, 13, False, "dirty"), (9, 12, True, "dirty")])
 def test_attention_naive_matches_torch_sdpa(S, T, causal, K):
     B, n_h = 2, 3
     q, k, v = _naive_problem(61 + S + T, B, S, T, n_h)
     allowed = np.ones((B, S, T), bool)
     idx = None
-    if K:
+    if K == "dirty":
+        # repeats and entries outside [0, T) (the reading of the scatter as a
+        # set); each query's own position is listed so none is left empty
+        g = rng(64)
+        idx = _dirty_sets(g, B * S, T, 10, n_bad=3, n_rep=2).reshape(B, S, 10)
+        for b in range(B):
+            for s in range(S):
+                idx[b, s, g.integers(10)] = T - S + s
+        allowed = _set_mask(idx, T)
+    elif K:
         g = rng(62)
         # every query keeps at least one visible key: the last row of the set
         # is its own position
