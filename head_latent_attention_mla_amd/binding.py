@@ -67,6 +67,8 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_step_workspace_bytes.restype = Z
         lib.mla_decode_step.argtypes = [P, P, P, P, P, L, L, L, L, I, I, I, I, P, I, I, F, I, P,
                                         P, P, Z, I, P]
+        lib.mla_decode_step_noalloc.argtypes = [P, P, P, P, P, L, L, L, L, I, I, I, I, P, I, I,
+                                                F, I, P, P, I, P]
         lib.mla_attention_naive_workspace_bytes.argtypes = [I, I, I, I]
         lib.mla_attention_naive_workspace_bytes.restype = Z
         lib.mla_attention_naive.argtypes = [P, P, P, I, I, I, I, P, I, I, F, P, P, P, Z, I, P]
@@ -74,7 +76,7 @@ def library() -> ctypes.CDLL:
                                          P]
         for name in ("mla_dequant_fp8_block", "mla_absorb_q", "mla_decode_latent_attn",
                      "mla_out_up", "mla_kv_reconstruct", "mla_cache_append",
-                     "mla_decode_latent_attn_multi", "mla_decode_step",
+                     "mla_decode_latent_attn_multi", "mla_decode_step", "mla_decode_step_noalloc",
                      "mla_absorb_q_packed", "mla_decode_latent_attn_packed",
                      "mla_attention_naive"):
             getattr(lib, name).restype = I
@@ -405,6 +407,47 @@ def mla_decode_step(q_nope: torch.Tensor, q_pe: torch.Tensor, wkv_b: torch.Tenso
         S_q, n_h, T, _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out),
         _ptr(lse), _ptr(workspace), ws_bytes, _dtype_code(q_nope), _stream(stream)))
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def mla_decode_step_noalloc(q_nope: torch.Tensor, q_pe: torch.Tensor, wkv_b: torch.Tensor,
+                            latent: torch.Tensor, rope: torch.Tensor, out: torch.Tensor,
+                            T: int = None, topk_idx: torch.Tensor = None, causal: bool = False,
+                            scale: float = SCALE, num_splits: int = 0, lse: torch.Tensor = None,
+                            stream=None) -> torch.Tensor:
+    """mla_decode_step with its workspace in the library's fixed per-GPU
+    scratch array (64 MiB): the caller passes inputs and outputs only (out is
+    required; nothing is allocated here or in the library). Calls that
+    overlap on one GPU share the scratch and race."""
+    _dev(q_nope, q_pe, wkv_b, latent, rope, topk_idx, out, lse)
+    squeeze = q_nope.dim() == 3
+    if squeeze:
+        q_nope, q_pe = q_nope.unsqueeze(1), q_pe.unsqueeze(1)
+    _require(q_nope.dim() == 4 and q_nope.shape[3] == 128 and q_nope.is_contiguous(),
+             "q_nope must be contiguous [B, S_q, n_h, 128]")
+    B, S_q, n_h, _ = q_nope.shape
+    _require(q_pe.dtype == q_nope.dtype and q_pe.is_contiguous() and
+             tuple(q_pe.shape) == (B, S_q, n_h, 64), "q_pe must be contiguous [B, S_q, n_h, 64]")
+    _require(wkv_b.dtype == q_nope.dtype and wkv_b.is_contiguous() and
+             tuple(wkv_b.shape) == (n_h * 256, 512), "wkv_b must be contiguous [n_h*256, 512]")
+    _require(latent.dtype == q_nope.dtype and rope.dtype == q_nope.dtype, "dtype mismatch")
+    lbs, lrs = _cache_strides(latent, 512, "latent")
+    rbs, rrs = _cache_strides(rope, 64, "rope")
+    _require(latent.shape[0] >= B and rope.shape[0] >= B, "cache batch too small")
+    if T is None:
+        T = latent.shape[1]
+    _require(T <= latent.shape[1] and T <= rope.shape[1], "T exceeds the cache length")
+    K = _topk_arg(topk_idx, B)
+    shape = (B, n_h, 128) if squeeze else (B, S_q, n_h, 128)
+    _require(out is not None and out.dtype == q_nope.dtype and out.is_contiguous() and
+             tuple(out.shape) == shape, f"out must be given, contiguous {list(shape)}")
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * S_q * n_h,
+                 "lse must be contiguous float32 with B * S_q * n_h elements")
+    _check("mla_decode_step_noalloc", library().mla_decode_step_noalloc(
+        _ptr(q_nope), _ptr(q_pe), _ptr(wkv_b), _ptr(latent), _ptr(rope), lbs, lrs, rbs, rrs, B,
+        S_q, n_h, T, _ptr(topk_idx), K, int(bool(causal)), float(scale), num_splits, _ptr(out),
+        _ptr(lse), _dtype_code(q_nope), _stream(stream)))
+    return out
 
 
 def mla_out_up(out_lat: torch.Tensor, wkv_b: torch.Tensor, out: torch.Tensor = None,

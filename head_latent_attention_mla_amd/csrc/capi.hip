@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 
 #include "mla.h"
 #include "common.hpp"
@@ -342,12 +343,53 @@ size_t mla_decode_step_workspace_bytes(int B, int S_q, int n_h, int T, int K, in
   return 2 * lat + attn;
 }
 
-mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv_b,
-                           const void* latent, const void* rope, int64_t lat_bstride,
-                           int64_t lat_rstride, int64_t rope_bstride, int64_t rope_rstride, int B,
-                           int S_q, int n_h, int T, const int32_t* topk_idx, int K, int causal,
-                           float scale, int num_splits, void* out, float* lse, void* workspace,
-                           size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of mla_decode_step_noalloc: one fixed device array per GPU,
+// reserved when the library's code object is loaded and held until the
+// process ends. In host code `scratch` is only a stand-in for the symbol,
+// never a device address: kernels get the per-device address that
+// hipGetSymbolAddress reports.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+mla_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  mla_status st = from_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (st != MLA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d devices with scratch", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = from_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != MLA_OK) return st;
+    if (!p) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// The decode step. With from_scratch, workspace/ws_bytes are ignored and the
+// library's fixed scratch array is used: every argument is checked first
+// (against a stand-in workspace address), then the array's address on the
+// current device is looked up, and only then is anything enqueued.
+mla_status decode_step_impl(const void* q_nope, const void* q_pe, const void* wkv_b,
+                            const void* latent, const void* rope, int64_t lat_bstride,
+                            int64_t lat_rstride, int64_t rope_bstride, int64_t rope_rstride, int B,
+                            int S_q, int n_h, int T, const int32_t* topk_idx, int K, int causal,
+                            float scale, int num_splits, void* out, float* lse, void* workspace,
+                            size_t ws_bytes, mla_dtype dt, hipStream_t stream, bool from_scratch) {
   if (!dtype_ok(dt)) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (S_q < 1 || B < 0 || n_h < 1)
     return fail(MLA_ERR_INVALID_ARG, "B=%d S_q=%d n_h=%d", B, S_q, n_h);
@@ -367,6 +409,14 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
     return fail(MLA_ERR_INVALID_ARG, "arguments rejected (S_q * n_h above 65535 or num_splits=%d)",
                 num_splits);
   }
+  if (from_scratch) {
+    if (need > kNoAllocScratchBytes)
+      return fail(MLA_ERR_WORKSPACE,
+                  "the step needs %zu bytes of workspace; the fixed scratch holds %zu", need,
+                  kNoAllocScratchBytes);
+    workspace = reinterpret_cast<void*>(uintptr_t{256});  // stand-in for the checks
+    ws_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || ws_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? ws_bytes : static_cast<size_t>(0));
@@ -385,6 +435,20 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
                                  scale, num_splits, o_lat, lse, ws + 2 * lat, ws_bytes - 2 * lat,
                                  dt, &p, &empty, dt == MLA_BF16 && (S_q * n_h) % 128 == 0);
   if (st != MLA_OK) return st;
+  if (from_scratch) {
+    // every check has passed: the real workspace, then the same plan on it
+    void* sp = nullptr;
+    st = scratch_of_current_device(&sp);
+    if (st != MLA_OK) return st;
+    ws = static_cast<char*>(sp);
+    q_lat = ws;
+    o_lat = ws + lat;
+    st = decode_prepare(q_lat, q_pe, latent, rope, lat_bstride, lat_rstride, rope_bstride,
+                        rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale, num_splits,
+                        o_lat, lse, ws + 2 * lat, ws_bytes - 2 * lat, dt, &p, &empty,
+                        dt == MLA_BF16 && (S_q * n_h) % 128 == 0);
+    if (st != MLA_OK) return st;
+  }
   // full 128-row groups: q_lat goes to the workspace in the attention
   // kernel's operand order (each wave then loads one contiguous KiB per
   // k-step instead of 32 row pieces)
@@ -408,6 +472,33 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
   if (st != MLA_OK) return st;
   return from_hip(launch_out_up(o_lat, wkv_b, out, BS, n_h, dt == MLA_BF16, stream),
                   "out_up launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv_b,
+                           const void* latent, const void* rope, int64_t lat_bstride,
+                           int64_t lat_rstride, int64_t rope_bstride, int64_t rope_rstride, int B,
+                           int S_q, int n_h, int T, const int32_t* topk_idx, int K, int causal,
+                           float scale, int num_splits, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, mla_dtype dt, hipStream_t stream) {
+  return decode_step_impl(q_nope, q_pe, wkv_b, latent, rope, lat_bstride, lat_rstride,
+                          rope_bstride, rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale,
+                          num_splits, out, lse, workspace, ws_bytes, dt, stream, false);
+}
+
+mla_status mla_decode_step_noalloc(const void* q_nope, const void* q_pe, const void* wkv_b,
+                                   const void* latent, const void* rope, int64_t lat_bstride,
+                                   int64_t lat_rstride, int64_t rope_bstride,
+                                   int64_t rope_rstride, int B, int S_q, int n_h, int T,
+                                   const int32_t* topk_idx, int K, int causal, float scale,
+                                   int num_splits, void* out, float* lse, mla_dtype dt,
+                                   hipStream_t stream) {
+  return decode_step_impl(q_nope, q_pe, wkv_b, latent, rope, lat_bstride, lat_rstride,
+                          rope_bstride, rope_rstride, B, S_q, n_h, T, topk_idx, K, causal, scale,
+                          num_splits, out, lse, nullptr, 0, dt, stream, true);
 }
 
 mla_status mla_out_up(const void* out_lat, const void* wkv_b, void* out, int B, int n_h,

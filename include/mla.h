@@ -247,6 +247,34 @@ mla_status mla_decode_step(const void* q_nope, const void* q_pe, const void* wkv
                            size_t ws_bytes, mla_dtype dt, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_decode_step with its workspace in a fixed device array of the library
+ * instead of a caller buffer. Arguments and results are those of
+ * mla_decode_step without workspace/ws_bytes; the kernels, and so the
+ * results bit for bit, are the same.
+ *   - The array holds 64 MiB (67108864 bytes) on each GPU the call runs on,
+ *     reserved when the library's code is loaded there and held until the
+ *     process ends. A call whose mla_decode_step_workspace_bytes exceeds it
+ *     returns MLA_ERR_WORKSPACE before anything is enqueued (B = 32, n_h =
+ *     128, T = 4096 needs about 40 MiB).
+ *   - The call allocates and frees nothing. Its first call on a device
+ *     looks up the array's address there (hipGetSymbolAddress, with the
+ *     device current); make that first call outside graph capture.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or concurrent graph replays) race
+ *     and give wrong results. Nothing in the array needs to start at zero:
+ *     each call writes what it reads.
+ */
+mla_status mla_decode_step_noalloc(const void* q_nope, const void* q_pe, const void* wkv_b,
+                                   const void* latent, const void* rope, int64_t lat_bstride,
+                                   int64_t lat_rstride, int64_t rope_bstride,
+                                   int64_t rope_rstride, int B, int S_q, int n_h, int T,
+                                   const int32_t* topk_idx, int K, int causal, float scale,
+                                   int num_splits, void* out, float* lse, mla_dtype dt,
+                                   hipStream_t stream);
+
+/*
  * W^UV after the probability-weighted sum ([KVR] "How it works", second
  * absorb identity, and "Watch-outs": attend on the latent, then W^UV;
  * [ABS] excerpt, last einsum; [VUP] "Explanation": value rows are 128..255

@@ -156,6 +156,23 @@ def test_multi_token_argument_errors(lib):
     assert need >= 2 * (2 * 2 * 128 * 512 * 2) + binding.mla_decode_workspace_bytes(2, 256, 4096)
 
 
+def test_noalloc_step_argument_errors(lib):
+    # every check runs before the scratch is looked up or anything enqueued
+    fn = lib.mla_decode_step_noalloc
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 64 * 576, 576, 64 * 576, 576, 512, 1, 128, 64,
+            None, 0, 0, 0.07, 0, FAKE, None, BF16, None]
+    assert fn(*args) == WORKSPACE          # 2 x 64 MiB of q_lat / out_lat: beyond the scratch
+    assert b"scratch" in lib.mla_last_error()
+    bad = list(args); bad[0] = None
+    assert fn(*bad) == INVALID
+    bad = list(args); bad[16] = float("nan")
+    assert fn(*bad) == WORKSPACE           # the size check comes first
+    bad = list(args); bad[9] = 2; bad[16] = float("nan")
+    assert fn(*bad) == INVALID             # within the scratch: the scale is checked
+    bad = list(args); bad[9] = 0; bad[0] = None
+    assert fn(*bad) == OK                  # empty batch: no-op
+
+
 def test_packed_query_argument_errors(lib):
     # packed queries exist for bf16 and whole 128-row groups only
     assert lib.mla_absorb_q_packed(FAKE, FAKE, FAKE, 2, 1, 64, BF16, None) == UNSUPPORTED
