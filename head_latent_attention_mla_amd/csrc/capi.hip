@@ -36,13 +36,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dtype_ok(mla_dtype dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
 // Split plan of the decode call: rows are cut into 32-row tiles, splits get
-// equal tile counts. Automatic choice: aim at one workgroup (8 waves, nearly
-// all of the LDS) per compute unit (256 on MI355X) without making any split
-// empty.
+// equal tile counts. Automatic choice: aim at one workgroup (nearly all of
+// the LDS) per compute unit (256 on MI355X) without making any split empty.
+// Dense rows: workgroups of 128 heads. Top-k rows: workgroups of 64 heads and
+// splits of whole 64-row iterations.
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxSplits = 1024;
 // The top-k kernel stages one split's indices in LDS: at most 1024 rows.
 constexpr int kMaxSparseTilesPerSplit = 1024 / 32;
+
+int group_heads(bool sparse) { return sparse ? 64 : 128; }
 
 struct SplitPlan {
   int num_splits;
@@ -54,17 +57,23 @@ struct SplitPlan {
 bool plan_splits(int B, int n_h, int rows, bool sparse, int requested, SplitPlan* out) {
   const int ntiles = (rows + 31) / 32;
   const int min_s = sparse ? (ntiles + kMaxSparseTilesPerSplit - 1) / kMaxSparseTilesPerSplit : 1;
-  int s = requested;
-  if (s == 0) {
-    const long base = static_cast<long>(B) * ((n_h + 127) / 128);
+  int tps;
+  if (requested == 0) {
+    const int gh = group_heads(sparse);
+    const long base = static_cast<long>(B) * ((n_h + gh - 1) / gh);
+    const int unit = sparse ? 2 : 1;  // tiles per iteration of the kernel
+    const int nunits = (ntiles + unit - 1) / unit;
     long want = (kTargetWorkgroups + base - 1) / base;
     if (want < 1) want = 1;
-    s = static_cast<int>(want < ntiles ? want : ntiles);
+    int s = static_cast<int>(want < nunits ? want : nunits);
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < min_s) s = min_s;
+    // whole iterations; at most 32 tiles per split when s >= min_s
+    tps = unit * ((nunits + s - 1) / s);
+  } else {
+    if (requested < min_s || requested > ntiles) return false;
+    tps = (ntiles + requested - 1) / requested;
   }
-  if (s < min_s || s > ntiles) return false;
-  const int tps = (ntiles + s - 1) / s;
   out->tiles_per_split = tps;
   out->num_splits = (ntiles + tps - 1) / tps;  // no empty split
   return true;
@@ -213,7 +222,8 @@ mla_status decode_prepare(const void* q_lat, const void* q_pe, const void* laten
                 sparse ? ((rows + 31) / 32 + kMaxSparseTilesPerSplit - 1) / kMaxSparseTilesPerSplit
                        : 1,
                 (rows + 31) / 32);
-  if (static_cast<int64_t>(sp.num_splits) * ((n_h + 127) / 128) * B > INT32_MAX)
+  if (static_cast<int64_t>(sp.num_splits) * ((n_h + group_heads(sparse) - 1) / group_heads(sparse)) * B >
+      INT32_MAX)
     return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 workgroups");
   if (sp.num_splits > 1 && static_cast<int64_t>(B) * n_h > (int64_t{1} << 26))
     return fail(MLA_ERR_UNSUPPORTED, "B * n_h above 2^26 with split rows");

@@ -40,6 +40,8 @@
 //
 // fp32 kernel: a plain per-(sequence, head, split) VALU kernel used for the
 // float32 interface (a correctness path, not a performance path).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -218,9 +220,9 @@ __device__ __forceinline__ floatx16 partial_scores(const char* buf, int s_off, c
 // FULL: every 128-head group holds 128 real heads (n_h % 128 == 0), which
 // removes the code for head quarters without heads.
 // CAUSAL (dense only): per-head visible row limit of multi-token queries.
-template <bool SPARSE, bool FULL, bool CAUSAL>
+template <bool FULL, bool CAUSAL>
 __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParams p) {
-  static_assert(!(SPARSE && CAUSAL), "the causal limit is for dense attention");
+  constexpr bool SPARSE = false;  // top-k rows go to attend64_bf16_kernel
   __shared__ __attribute__((aligned(16))) char tiles[NBUF * BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float sx[4 * 16 * 64];  // partner partial scores
   __shared__ __attribute__((aligned(16))) u32x4 qpe[4 * 4 * 64];  // rotary query operands
@@ -228,9 +230,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   __shared__ float fac[128];                                       // rescale factor per head
   __shared__ __attribute__((aligned(16))) int flag[4];             // head quarter rescaled
   __shared__ float linv[128];                                      // 1 / sum per head
-  __shared__ int idx_lds[SPARSE ? MAX_SPARSE_ROWS : 1];
-  // bit r of word k: row 32k + r of this split is a position of the index set
-  __shared__ uint32_t vmask[SPARSE ? MAX_SPARSE_ROWS / 32 : 1];
+  const int* const idx_lds = nullptr;  // (no index rows: dense attention)
 
   // Workgroups are dealt to the 8 XCDs round-robin in launch order. Renumber
   // them so that the splits of one (sequence, head group) run on one XCD and
@@ -268,26 +268,6 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   const uint32_t rope_rb = static_cast<uint32_t>(p.rope_rs * 2);
   const uint32_t tiles_addr = __builtin_amdgcn_readfirstlane(lds_addr(tiles));
 
-  if (SPARSE) {
-    // The index set is a scatter into a -inf row: an entry outside [0, T)
-    // addresses no position. Such entries are staged as row 0 (so every
-    // fetch stays inside the cache) and cleared in vmask (weight zero).
-    const int* src = p.idx + static_cast<int64_t>(b) * p.K + row_begin;
-    const int n_rows = row_end - row_begin;
-    for (int i0 = 0; i0 < n_rows; i0 += NWAVES * 64) {
-      const int i = i0 + threadIdx.x;
-      const int v = i < n_rows ? src[i] : -1;
-      const bool ok = v >= 0 && v < p.T;
-      if (i < n_rows) idx_lds[i] = ok ? v : 0;
-      const uint64_t bal = __ballot(ok);
-      // i is a multiple of 64 on lane 0: words i/32 and i/32 + 1
-      if (lane == 0 && i < MAX_SPARSE_ROWS) {
-        vmask[i >> 5] = static_cast<uint32_t>(bal);
-        vmask[(i >> 5) + 1] = static_cast<uint32_t>(bal >> 32);
-      }
-    }
-    __syncthreads();
-  }
   // prologue DMA of tile 0; the query loads that follow are waited for
   // (by the compiler) before the rest of the prologue DMA is issued
   issue_tile<SPARSE>(lat_d, rope_d, lat_rb, rope_rb, idx_lds, row_begin, row_end, row_begin,
@@ -501,13 +481,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       // partial scores of tile it+1 (on the last tile they read a stale
       // buffer and are discarded); the partner's multiplies fill the
       // SIMD's MFMA pipe meanwhile ----
-      if (SPARSE) {
-        // rows of this lane: tile rows 16g..16g+15 (rows past the split are
-        // clear in vmask too)
-        const uint32_t bits = vmask[it] >> (16 * g);
-#pragma unroll
-        for (int r = 0; r < 16; r++) S[r] = (bits >> r) & 1u ? S[r] : -INFINITY;
-      } else {
+      {
         const int valid = row_vis - (row_begin + it * TILE);  // visible rows of this tile
 #pragma unroll
         for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
@@ -520,9 +494,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       const bool rescaled = __any(tmax > m + RESCALE_SLACK);
       const float m_new = rescaled ? fmaxf(m, tmax) : m;
       // 0 on the first tile; a head that has seen no visible row yet (causal
-      // limit, or index entries outside [0, T)) keeps m = -inf, factor 1 and
-      // weights exp2(-inf) = 0
-      constexpr bool MAYBE_EMPTY = CAUSAL || SPARSE;
+      // limit) keeps m = -inf, factor 1 and weights exp2(-inf) = 0
+      constexpr bool MAYBE_EMPTY = CAUSAL;
       const float f = rescaled && (!MAYBE_EMPTY || m_new != -INFINITY)
                           ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
       l *= f;
@@ -588,7 +561,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
   if (kh == 1 && active) {
     const float l_tot = pair_sum(l);
     // a head with no visible row in this split: zero partial, lse -inf
-    if (g == 0) linv[hq * 32 + n] = !(CAUSAL || SPARSE) || l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (g == 0) linv[hq * 32 + n] = !CAUSAL || l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (g == 0 && head < p.n_h) {
       const float lse_v = (m + log2f(l_tot)) * LN2;  // natural log of sum exp(z)
       const int64_t bh = static_cast<int64_t>(b) * p.n_h + head;
@@ -621,6 +594,385 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       st16(o, v0);
       st16(o + 8, v1);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel for top-k rows, 64 heads per workgroup. A top-k split holds few
+// rows (config B=8, K=2048: 128 per workgroup), so what a workgroup reads
+// and writes besides its gathered rows matters: with 64 heads it loads half
+// the queries and writes half the partial output of a 128-head workgroup,
+// and the split merge reads half as much. (For dense rows the 128-head
+// kernel above is faster: one wave per SIMD here leaves the LDS latency and
+// the softmax exposed, which two waves per SIMD hide.)
+// One workgroup of 4 waves (one per SIMD) per (sequence, group of 64 heads,
+// split of the index rows). Each iteration stages 64 gathered rows (two
+// 32-row halves, each laid out as a tile above) into one of two LDS buffers
+// by LDS-DMA while the other is consumed; the rows of the iteration after
+// that are touched once with plain loads so they are in flight to L2.
+// Wave (ph, hb): head block hb (32 heads), row half ph.
+//   scores   S^T[32 rows x 32 heads] of its row half in one 576-deep MFMA
+//            chain (all 36 query k-steps of its heads held in registers);
+//   softmax  the two row-half waves of a head block share one running max:
+//            each publishes its tile maximum, both take the larger, so both
+//            hold the same max and the same rescale decisions; each turns
+//            its own rows into P (bf16, MFMA operand layout) and hands them
+//            to the other through the rotary region of its half (free once
+//            every wave's scores are done);
+//   mix      O^T[256 x 32 heads] += C^T[256 x 64 rows] . P^T over latent
+//            features [256 ph, 256 ph + 256) and both row halves.
+// Three barriers per iteration: tile resident, maxima published, P
+// published.
+constexpr int A4_HEADS = 64;
+constexpr int A4_WAVES = 4;
+constexpr int A4_HALF = BUF_BYTES;       // 32 rows (latent + rotary)
+constexpr int A4_ITER = 2 * BUF_BYTES;   // 64 rows
+constexpr int A4_STEPS = TILE / A4_WAVES + 1;  // DMA instructions per wave and half
+#ifndef MLA_A4_SRING
+#define MLA_A4_SRING 4
+#endif
+#ifndef MLA_A4_MRING
+#define MLA_A4_MRING 1
+#endif
+#ifndef MLA_A4_PF_LOADS
+#define MLA_A4_PF_LOADS 3
+#endif
+constexpr int A4_PF_LOADS = MLA_A4_PF_LOADS;  // L2 prefetch loads per wave and iteration
+constexpr int A4_SRING = MLA_A4_SRING;  // score operands read ahead
+constexpr int A4_MRING = MLA_A4_MRING;  // mix feature blocks read ahead
+
+__global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeParams p) {
+  constexpr bool SPARSE = true;
+  __shared__ __attribute__((aligned(16))) char tiles[2 * A4_ITER];
+  __shared__ float xmax[A4_WAVES * 64];  // published tile maxima
+  __shared__ int idx_lds[MAX_SPARSE_ROWS];
+  // bit r of word k: row 32k + r of this split is a position of the index set
+  __shared__ uint32_t vmask[MAX_SPARSE_ROWS / 32];
+
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order. Renumber
+  // them so that the splits and head groups of one sequence run on one XCD:
+  // the head groups of a split read the same rows, which the second then
+  // finds in that XCD's L2.
+  int s, hg, b;
+  {
+    const int S = gridDim.x, HG = gridDim.y;
+    const int G = S * HG * gridDim.z;
+    const int L = blockIdx.x + S * (blockIdx.y + HG * blockIdx.z);
+    const int j = (G & 7) == 0 ? (L & 7) * (G >> 3) + (L >> 3) : L;
+    s = j % S;
+    hg = (j / S) % HG;
+    b = j / (S * HG);
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int ph = wave >> 1;      // row half of every iteration, and feature half of the mix
+  const int hb = wave & 1;       // head block of the group
+  const int hblk = hg * 2 + hb;  // global 32-head block
+  const int head = hblk * 32 + n;
+  const int headc = min(head, p.n_h - 1);
+
+  const int row_begin = s * p.tiles_per_split * TILE;
+  const int row_end = min(p.rows, row_begin + p.tiles_per_split * TILE);
+  const int niter = (row_end - row_begin + 2 * TILE - 1) / (2 * TILE);
+
+  const i32x4 lat_d =
+      make_rsrc(static_cast<const uint16_t*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs);
+  const i32x4 rope_d =
+      make_rsrc(static_cast<const uint16_t*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs);
+  const uint32_t lat_rb = static_cast<uint32_t>(p.lat_rs * 2);
+  const uint32_t rope_rb = static_cast<uint32_t>(p.rope_rs * 2);
+  const uint32_t tiles_addr = __builtin_amdgcn_readfirstlane(lds_addr(tiles));
+
+  {
+    // The index set is a scatter into a -inf row: an entry outside [0, T)
+    // addresses no position. Such entries are staged as row 0 (so every
+    // fetch stays inside the cache) and cleared in vmask (weight zero).
+    const int* src = p.idx + static_cast<int64_t>(b) * p.K + row_begin;
+    const int n_rows = row_end - row_begin;
+    for (int i0 = 0; i0 < n_rows; i0 += A4_WAVES * 64) {
+      const int i = i0 + threadIdx.x;
+      const int v = i < n_rows ? src[i] : -1;
+      const bool ok = v >= 0 && v < p.T;
+      if (i < n_rows) idx_lds[i] = ok ? v : 0;
+      const uint64_t bal = __ballot(ok);
+      if (lane == 0 && i < MAX_SPARSE_ROWS) {  // i is a multiple of 64 on lane 0
+        vmask[i >> 5] = static_cast<uint32_t>(bal);
+        vmask[(i >> 5) + 1] = static_cast<uint32_t>(bal >> 32);
+      }
+    }
+    __syncthreads();
+  }
+  // DMA step k (0 .. 2*A4_STEPS-1) of this wave for iteration it: half
+  // k / A4_STEPS, step k % A4_STEPS of that half. A half past the split's
+  // rows is filled with copies of its last row: its weights are zero, and
+  // the mix must not multiply them by stale (possibly non-finite) bytes.
+  // With a zero-range descriptor (no next iteration) every load of a step is
+  // out of range: nothing is fetched and zeros land in the free buffer, so
+  // the steps need no branch between the score multiplies.
+  i32x4 lat_z = lat_d, rope_z = rope_d;
+  lat_z[2] = 0;
+  rope_z[2] = 0;
+  auto stage = [&](int it, int k, bool live) {
+    const int half = k / A4_STEPS;
+    const int row0 = min(row_begin + it * 2 * TILE + half * TILE, row_end - 1);
+    i32x4 ld = lat_d, rd = rope_d;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      ld[e] = live ? lat_d[e] : lat_z[e];
+      rd[e] = live ? rope_d[e] : rope_z[e];
+    }
+    stage_step<SPARSE, A4_WAVES>(k % A4_STEPS, ld, rd, lat_rb, rope_rb, idx_lds, row0, row_end,
+                                 row_begin, tiles_addr + (it & 1) * A4_ITER + half * A4_HALF,
+                                 wave, lane);
+  };
+#pragma unroll
+  for (int k = 0; k < 2 * A4_STEPS; k++) stage(0, k, true);
+
+  // L2 prefetch of iteration it: wave w touches the 9 lines (8 latent, 1
+  // rotary) of rows [16w, 16w + 16) of that iteration with A4_PF_LOADS
+  // 4-byte loads per lane (rows past the split re-read its last row). The
+  // LDS buffers hold one iteration ahead; these loads put the next one in
+  // flight too, so the staging DMA later finds its lines in L2. Their
+  // values are only folded into `sink`, PF iterations later, when the
+  // loads have long completed.
+  const uint16_t* lat_b = static_cast<const uint16_t*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs;
+  const uint16_t* rope_b = static_cast<const uint16_t*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs;
+  auto prefetch = [&](int it, int k) -> uint32_t {
+    const int L = 64 * k + lane;
+    const int rr = min(L / 9, 15), ln = L - (L / 9) * 9;
+    int row = min(row_begin + it * 2 * TILE + 16 * wave + rr, row_end - 1);
+    row = idx_lds[row - row_begin];
+    const uint16_t* a = ln < 8 ? lat_b + static_cast<int64_t>(row) * p.lat_rs + 64 * ln
+                               : rope_b + static_cast<int64_t>(row) * p.rope_rs;
+    return *reinterpret_cast<const uint32_t*>(a);
+  };
+  uint32_t pf_old[A4_PF_LOADS], pf_pend[A4_PF_LOADS];
+#pragma unroll
+  for (int k = 0; k < A4_PF_LOADS; k++) pf_old[k] = 0u;
+
+  // queries of this lane's head: 32 latent k-steps (rows layout: features
+  // 16ks + 8g of the row; operand order: one contiguous KiB per k-step and
+  // 32-head block) and the 4 rotary k-steps
+  const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
+  bf16x8 q[D_QK / 16];
+  {
+    const uint16_t* ql;
+    int step;
+    if (p.q_swz) {
+      ql = static_cast<const uint16_t*>(p.q_lat) +
+           ((static_cast<int64_t>(b) * (p.n_h >> 7) + (hblk >> 2)) * 4 + (hblk & 3)) * (32 * 512) +
+           8 * lane;
+      step = 512;
+    } else {
+      ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
+      step = 16;
+    }
+#pragma unroll
+    for (int j = 0; j < D_C / 16; j++) q[j] = as_bf16x8(ld16(ql + step * j));
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R + 8 * g;
+#pragma unroll
+    for (int j = 0; j < D_R / 16; j++) q[D_C / 16 + j] = as_bf16x8(ld16(qp + 16 * j));
+  }
+#pragma unroll
+  for (int k = 0; k < A4_PF_LOADS; k++) pf_pend[k] = prefetch(1, k);
+  uint32_t sink = 0u;
+
+  // per-lane LDS byte offsets inside a 32-row half (tile-independent)
+  const int srow = pi_row(n);
+  const int s_off = srow * LAT_PITCH + 16 * (lat_shift(srow) + g);
+  const int r_off = LAT_BYTES + srow * 128;
+  const int r_x = g ^ swz_rope(srow);
+  int m_off;  // transposing reads of this wave's feature half
+  {
+    const int tau = tau_blk(4 * ((lane >> 4) & 1) + (lane & 3));
+    const int row0 = 16 * g + ((lane & 15) >> 2);
+    m_off = row0 * LAT_PITCH + 16 * (2 * g + (tau >> 1)) + 8 * (tau & 1) + 512 * ph;
+  }
+
+  constexpr int NFB = D_C / 2 / 32;  // 8 feature blocks of 32 per wave
+  floatx16 O[NFB];                   // O^T accumulators: feature block, this lane's head
+#pragma unroll
+  for (int i = 0; i < NFB; i++) O[i] = floatx16{};
+  float m = -INFINITY;  // running max of scale*log2(e)*score (shared with the other row half)
+  float l = 0.f;        // this lane's share of the running sum (both row halves)
+  const float sl2 = p.scale * LOG2E;
+  constexpr int NKS = D_QK / 16;  // 36 k-steps
+
+  for (int it = 0; it < niter; it++) {
+    // buffer it & 1 complete (this wave's DMA, then everyone's; only the
+    // A4_PF_LOADS prefetches issued after it may still be in flight); every
+    // wave is done with iteration it-1, whose buffer the DMA of it+1
+    // overwrites
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(A4_PF_LOADS) : "memory");
+    __syncthreads();
+    // prefetches issued two iterations ago have completed
+#pragma unroll
+    for (int k = 0; k < A4_PF_LOADS; k++) {
+      sink ^= pf_old[k];
+      pf_old[k] = pf_pend[k];
+    }
+    const bool next = it + 1 < niter;
+    const int row0 = row_begin + it * 2 * TILE + ph * TILE;  // first row of this wave's half
+    const char* buf = tiles + (it & 1) * A4_ITER;
+    const char* half = buf + ph * A4_HALF;
+    // ---- scores: one 36-deep chain; the DMA of the next iteration and the
+    // L2 prefetch of the one after are issued between the first multiplies.
+    // Lanes of heads past n_h compute on clamped heads (every wave runs the
+    // same code; nothing of theirs is stored). ----
+    floatx16 S = {};
+    {
+      auto operand = [&](int j) -> u32x4 {
+        if (j < D_C / 16) return *reinterpret_cast<const u32x4*>(half + s_off + 32 * j);
+        return *reinterpret_cast<const u32x4*>(half + r_off +
+                                               (((2 * (j - D_C / 16)) ^ r_x) << 4));
+      };
+      u32x4 ring[A4_SRING];
+#pragma unroll
+      for (int j = 0; j < A4_SRING; j++) ring[j] = operand(j);
+#pragma unroll
+      for (int j = 0; j < NKS; j++) {
+        const u32x4 a = ring[j % A4_SRING];
+        if (j + A4_SRING < NKS) ring[j % A4_SRING] = operand(j + A4_SRING);
+        if (j < 2 * A4_STEPS) stage(it + 1, j, next);
+        if (j >= 2 * A4_STEPS && j < 2 * A4_STEPS + A4_PF_LOADS)
+          pf_pend[j - 2 * A4_STEPS] = prefetch(it + 2, j - 2 * A4_STEPS);
+        S = mfma32x32x16(as_bf16x8(a), q[j], S);
+      }
+    }
+    // ---- this half's visible rows and its maximum ----
+    {
+      // rows of this lane: 16g..16g+15 of its half (rows past the split are
+      // clear in vmask too)
+      const int w = (row0 - row_begin) >> 5;
+      const uint32_t bits = row0 < row_end ? vmask[w] >> (16 * g) : 0u;
+#pragma unroll
+      for (int r = 0; r < 16; r++) S[r] = (bits >> r) & 1u ? S[r] : -INFINITY;
+    }
+    float smax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r++) smax = fmaxf(smax, S[r]);
+    // scale > 0, so the max of the scaled scores is the scaled max
+    const float tmax_own = pair_max(smax * sl2);
+    xmax[wave * 64 + lane] = tmax_own;
+    __syncthreads();  // maxima published; every wave's scores are done
+    const float tmax = fmaxf(tmax_own, xmax[(wave ^ 2) * 64 + lane]);
+    const bool rescaled = __any(tmax > m + RESCALE_SLACK);
+    const float m_new = rescaled ? fmaxf(m, tmax) : m;
+    // 0 on the first visible rows; a head that has seen no visible row yet
+    // keeps m = -inf, factor 1 and weights exp2(-inf) = 0
+    const float f = rescaled && m_new != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+    l *= f;
+    m = m_new;
+    const float nm = m != -INFINITY ? -m : 0.f;
+    u32x4 Pown[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+#pragma unroll
+      for (int w2 = 0; w2 < 4; w2++) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * kk + 2 * w2], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * kk + 2 * w2 + 1], sl2, nm));
+        Pown[kk][w2] = pack_bf16x2(p0, p1);
+      }
+    }
+    // P of this half into its rotary region (read by the scores only)
+    u32x4* const pw = reinterpret_cast<u32x4*>(const_cast<char*>(half) + LAT_BYTES);
+    pw[hb * 128 + lane] = Pown[0];
+    pw[hb * 128 + 64 + lane] = Pown[1];
+    __syncthreads();  // P published
+    const u32x4* const po =
+        reinterpret_cast<const u32x4*>(buf + (1 - ph) * A4_HALF + LAT_BYTES) + hb * 128;
+    u32x4 P[2][2];  // [row half][k-step]
+    P[ph][0] = Pown[0];
+    P[ph][1] = Pown[1];
+    P[1 - ph][0] = po[lane];
+    P[1 - ph][1] = po[64 + lane];
+    // the denominator sums the rounded weights the mix actually uses
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+        for (int w2 = 0; w2 < 4; w2++)
+          l += __uint_as_float(P[hh][kk][w2] << 16) +
+               __uint_as_float(P[hh][kk][w2] & 0xFFFF0000u);
+    // ---- mix: O^T[256 x 32 heads] += C^T[256 x 64 rows] . P^T; when the
+    // running max was raised each block is rescaled right before its first
+    // multiply (a second copy of the loop: the accumulators stay in the
+    // registers the multiplies use) ----
+    {
+      auto mixop = [&](int fb, int hh, int kk) -> bf16x8 {
+        const char* mp = buf + hh * A4_HALF + m_off + 8704 * kk + 64 * fb;
+        return tr_pair(mp, mp + 4368);
+      };
+      auto mix = [&](auto rescale) {
+        bf16x8 A[A4_MRING][4];
+#pragma unroll
+        for (int j = 0; j < A4_MRING; j++)
+#pragma unroll
+          for (int c = 0; c < 4; c++) A[j][c] = mixop(j, c >> 1, c & 1);
+#pragma unroll
+        for (int fb = 0; fb < NFB; fb++) {
+          bf16x8 a[4];
+#pragma unroll
+          for (int c = 0; c < 4; c++) a[c] = A[fb % A4_MRING][c];
+          if (fb + A4_MRING < NFB) {
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+              A[fb % A4_MRING][c] = mixop(fb + A4_MRING, c >> 1, c & 1);
+          }
+          if (decltype(rescale)::value) {
+            floatx16 t = O[fb] * f;
+            // back into accumulation registers, so that the multiplies below
+            // (and so both copies of the loop) keep O in the same registers
+            asm volatile("" : "+a"(t));
+            O[fb] = t;
+          }
+#pragma unroll
+          for (int c = 0; c < 4; c++)
+            O[fb] = mfma32x32x16(a[c], as_bf16x8(P[c >> 1][c & 1]), O[fb]);
+        }
+      };
+      if (rescaled)
+        mix(std::true_type{});
+      else
+        mix(std::false_type{});
+    }
+  }
+
+  // the prefetched values are never needed; this keeps the loads (a sink
+  // of all ones bits would need a cache of all-ones rows and a negative B)
+  if (sink == 0xFFFFFFFFu && p.B < 0) p.lse[0] = 0.f;
+  // ---- epilogue: normalise and store features [256 ph, 256 ph + 256) ----
+  const float L = pair_sum(l);
+  // a head with no visible row in this split: zero partial, lse -inf
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
+  const int64_t bh = static_cast<int64_t>(b) * p.n_h + head;
+  if (ph == 0 && g == 0 && head < p.n_h) {
+    const float lse_v = (m + log2f(L)) * LN2;  // natural log of sum exp(z)
+    if (p.num_splits == 1) {
+      if (p.lse) p.lse[bh] = lse_v;
+    } else {
+      p.ws_lse[static_cast<int64_t>(s) * BH + bh] = lse_v;
+    }
+  }
+  if (head >= p.n_h) return;
+  uint16_t* out_base = p.num_splits == 1
+                           ? static_cast<uint16_t*>(p.out_lat)
+                           : static_cast<uint16_t*>(p.ws_o) + static_cast<int64_t>(s) * BH * D_C;
+  uint16_t* dst = out_base + bh * D_C + 256 * ph;
+#pragma unroll
+  for (int fb = 0; fb < NFB; fb++) {
+    u32x4 v0, v1;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; w2++) {
+      v0[w2] = pack_bf16x2(O[fb][2 * w2] * inv, O[fb][2 * w2 + 1] * inv);
+      v1[w2] = pack_bf16x2(O[fb][8 + 2 * w2] * inv, O[fb][8 + 2 * w2 + 1] * inv);
+    }
+    uint16_t* o = dst + 32 * fb + 16 * g;
+    st16(o, v0);
+    st16(o + 8, v1);
   }
 }
 
@@ -775,16 +1127,19 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream,
                          bool merge_splits) {
-  const int hgroups = (p.n_h + 127) / 128;
   if (is_bf16) {
-    dim3 grid(p.num_splits, hgroups, p.B);
-    const bool full = p.n_h % 128 == 0;
-    auto kern =
-        p.idx ? (full ? decode_bf16_kernel<true, true, false> : decode_bf16_kernel<true, false, false>)
-        : p.causal
-            ? (full ? decode_bf16_kernel<false, true, true> : decode_bf16_kernel<false, false, true>)
-            : (full ? decode_bf16_kernel<false, true, false> : decode_bf16_kernel<false, false, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(NWAVES * 64), 0, stream, p);
+    if (p.idx) {
+      // top-k rows: 64-head workgroups (fewer query and partial bytes per
+      // gathered row; see attend64_bf16_kernel)
+      dim3 grid(p.num_splits, (p.n_h + A4_HEADS - 1) / A4_HEADS, p.B);
+      hipLaunchKernelGGL(attend64_bf16_kernel, grid, dim3(A4_WAVES * 64), 0, stream, p);
+    } else {
+      dim3 grid(p.num_splits, (p.n_h + 127) / 128, p.B);
+      const bool full = p.n_h % 128 == 0;
+      auto kern = p.causal ? (full ? decode_bf16_kernel<true, true> : decode_bf16_kernel<false, true>)
+                           : (full ? decode_bf16_kernel<true, false> : decode_bf16_kernel<false, false>);
+      hipLaunchKernelGGL(kern, grid, dim3(NWAVES * 64), 0, stream, p);
+    }
   } else {
     hipLaunchKernelGGL(decode_f32_kernel, dim3(p.num_splits, p.n_h, p.B), dim3(256), 0, stream, p);
   }

@@ -103,10 +103,13 @@ def test_workspace_size_queries(lib):
     assert ws(2, 128, 4096, num_splits=8) < ws(2, 128, 4096, num_splits=16)
     with pytest.raises(binding.MLAError):
         ws(2, 128, 4096, K=5000)
+    # one workgroup per (sequence, head group, split), 256 in all: 128-head
+    # groups for dense rows, 64-head groups for top-k rows
     assert binding.mla_decode_num_splits(32, 128, 4096) == 8
     assert binding.mla_decode_num_splits(4, 128, 32768) == 64
-    assert binding.mla_decode_num_splits(8, 128, 65536, 2048) == 32
+    assert binding.mla_decode_num_splits(8, 128, 65536, 2048) == 16
     assert binding.mla_decode_num_splits(1, 16, 1) == 1
+    assert binding.mla_decode_num_splits(256, 128, 4096) == 1
 
 
 def test_reconstruct_argument_errors(lib):
