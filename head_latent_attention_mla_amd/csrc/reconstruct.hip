@@ -80,6 +80,16 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Output stores: whole 256-byte rows of one token and head (128-byte rows
+// for the rotary copy), non-temporal: the 671 MB of outputs at N = 8192 then
+// do not displace the weight and latent rows later tiles re-read from L2
+// (measured 323 against 362 us with ordinary stores; with the 16-byte
+// pieces of the MFMA layout, non-temporal stores were slower, since L2 then
+// cannot merge the pieces of a line).
+__device__ __forceinline__ void rc_store(uint16_t* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt immediate out of range");
@@ -209,33 +219,60 @@ __global__ __launch_bounds__(256, 1) void kv_reconstruct_bf16_kernel(
           for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma32x32x16(av[mt], bv[nt], acc[mt][nt]);
       }
     });
-    // epilogue: lane (token n of N-tile nt, half g) holds features
-    // 32mt + 16g .. +15 of half wm; tail tokens rewrite the last token
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-      const int64_t tk = cur.tok0 + (min(wn * 128 + nt * 32 + n, cur.last_row));
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        const int e = mt * 32 + 16 * g;
-        u32x4 v0, v1;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; w2++) {
-          v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2], acc[mt][nt][2 * w2 + 1]);
-          v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2], acc[mt][nt][8 + 2 * w2 + 1]);
-        }
-        uint16_t* dst = wm == 0 ? Kout + (tk * n_h + cur.h) * (D_N + D_R) + e
-                                : Vout + (tk * n_h + cur.h) * D_V + e;
-        st16(dst, v0);
-        st16(dst + 8, v1);
-      }
-    }
     // K[n,h,128:192] = k_rope[n,:] from the staged rows: 8 chunks per token
 #pragma unroll
     for (int k = 0; k < RC_TOK * 8 / 256; k++) {
       const int idx = k * 256 + static_cast<int>(threadIdx.x);
       const int tl = min(idx >> 3, cur.last_row);
       const u32x4 v = ld_lds16(rope_buf + (idx >> 3) * 128 + (idx & 7) * 16);
-      st16(Kout + ((cur.tok0 + tl) * n_h + cur.h) * (D_N + D_R) + D_N + (idx & 7) * 8, v);
+      rc_store(Kout + ((cur.tok0 + tl) * n_h + cur.h) * (D_N + D_R) + D_N + (idx & 7) * 8, v);
+    }
+    // every wave is done with the rotary rows: the buffer now stages each
+    // wave's outputs (8 KB per wave), so that every store instruction writes
+    // whole 256-byte rows (4 tokens) instead of 64 separate 16-byte pieces.
+    // The buffer is next written by the rotary DMA issued after the barrier
+    // of the next tile's stage 1.
+    __syncthreads();
+    char* stg = const_cast<char*>(rope_buf) + wave * 8192;
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+      // lane (token n of N-tile nt, half g) holds features 32mt + 16g .. +15
+      // of half wm: chunks 4mt + 2g, +1 of the token's 16-chunk row,
+      // XOR-swizzled by token
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        u32x4 v0, v1;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; w2++) {
+          v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2], acc[mt][nt][2 * w2 + 1]);
+          v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2], acc[mt][nt][8 + 2 * w2 + 1]);
+        }
+        const int c0 = 4 * mt + 2 * g;
+        *reinterpret_cast<u32x4*>(stg + n * 256 + ((c0 ^ (n & 15)) << 4)) = v0;
+        *reinterpret_cast<u32x4*>(stg + n * 256 + (((c0 + 1) ^ (n & 15)) << 4)) = v1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // 16 lanes per token row: tokens 4i + lane/16, chunk lane % 16; tail
+      // tokens rewrite the last token's row with identical values
+      u32x4 rows[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int r = 4 * i + (lane >> 4), c = lane & 15;
+        rows[i] = ld_lds16(stg + r * 256 + ((c ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int r = 4 * i + (lane >> 4), c = lane & 15;
+        const int64_t tk = cur.tok0 + min(wn * 128 + nt * 32 + r, cur.last_row);
+        uint16_t* dst = wm == 0 ? Kout + (tk * n_h + cur.h) * (D_N + D_R) + c * 8
+                                : Vout + (tk * n_h + cur.h) * D_V + c * 8;
+        rc_store(dst, rows[i]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     cur = nxt;
   }
