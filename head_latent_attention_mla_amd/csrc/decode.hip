@@ -631,15 +631,11 @@ constexpr int A4_STEPS = TILE / A4_WAVES + 1;  // DMA instructions per wave and 
 #ifndef MLA_A4_SRING
 #define MLA_A4_SRING 4
 #endif
-#ifndef MLA_A4_MRING
-#define MLA_A4_MRING 1
-#endif
 #ifndef MLA_A4_PF_LOADS
 #define MLA_A4_PF_LOADS 3
 #endif
 constexpr int A4_PF_LOADS = MLA_A4_PF_LOADS;  // L2 prefetch loads per wave and iteration
 constexpr int A4_SRING = MLA_A4_SRING;  // score operands read ahead
-constexpr int A4_MRING = MLA_A4_MRING;  // mix feature blocks read ahead
 
 __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeParams p) {
   constexpr bool SPARSE = true;
@@ -713,21 +709,67 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
   i32x4 lat_z = lat_d, rope_z = rope_d;
   lat_z[2] = 0;
   rope_z[2] = 0;
-  auto stage = [&](int it, int k, bool live) {
-    const int half = k / A4_STEPS;
-    const int row0 = min(row_begin + it * 2 * TILE + half * TILE, row_end - 1);
+  // Row indices of an iteration's staging and prefetch, read from idx_lds
+  // in a few loads at the top of the iteration before the score multiplies:
+  // an index read inside the multiply chain would make its wait (the LDS
+  // counter is in order) wait for every tile operand read issued before it.
+  //   lat   lane j < 16: the global row of latent step (half j / 8, k j % 8),
+  //         i.e. tile row 4k + wave of that half (handed out by readlane);
+  //   rope  the row of this lane's rotary chunk in half 0 / 1;
+  //   pf    the row of this lane's prefetch line k.
+  struct Rows {
+    int lat, rope[2], pf[A4_PF_LOADS];
+  };
+  auto rows_of = [&](int it) {
+    Rows r;
+    auto grow = [&](int half, int R) {  // index-set row R of a half (clamped)
+      const int row0 = min(row_begin + it * 2 * TILE + half * TILE, row_end - 1);
+      const int valid = row_end - row0;
+      return idx_lds[row0 - row_begin + (R < valid ? R : valid - 1)];
+    };
+    r.lat = grow((lane >> 3) & 1, 4 * (lane & 7) + wave);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) r.rope[h2] = grow(h2, 8 * wave + (lane >> 3));
+#pragma unroll
+    for (int k = 0; k < A4_PF_LOADS; k++) {
+      const int L = 64 * k + lane;
+      const int row = min(row_begin + it * 2 * TILE + 16 * wave + min(L / 9, 15), row_end - 1);
+      r.pf[k] = idx_lds[row - row_begin];
+    }
+    return r;
+  };
+  // DMA step k (0 .. 2*A4_STEPS-1) of this wave for iteration it into buffer
+  // it & 1: half k / A4_STEPS; steps 0..7 of a half stage latent rows
+  // 4k + wave, step 8 the rotary rows 8 wave .. 8 wave + 7 (8 lanes per row).
+  // A half past the split's rows holds copies of its last row (weights zero;
+  // the mix must not multiply them by stale, possibly non-finite, bytes).
+  auto stage = [&](int it, int k, bool live, const Rows& r) {
+    const int half = k / A4_STEPS, kk = k % A4_STEPS;
     i32x4 ld = lat_d, rd = rope_d;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       ld[e] = live ? lat_d[e] : lat_z[e];
       rd[e] = live ? rope_d[e] : rope_z[e];
     }
-    stage_step<SPARSE, A4_WAVES>(k % A4_STEPS, ld, rd, lat_rb, rope_rb, idx_lds, row0, row_end,
-                                 row_begin, tiles_addr + (it & 1) * A4_ITER + half * A4_HALF,
-                                 wave, lane);
+    const uint32_t dst = tiles_addr + (it & 1) * A4_ITER + half * A4_HALF;
+    if (kk < TILE / A4_WAVES) {
+      const int R = A4_WAVES * kk + wave;
+      const uint32_t grow =
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(r.lat, half * 8 + kk));
+      dma16(ld, dst + R * LAT_PITCH + 16 * lat_shift(R), static_cast<uint32_t>(lane * 16),
+            __builtin_amdgcn_readfirstlane(grow * lat_rb));
+    } else {
+      const int R = 8 * wave + (lane >> 3);
+      const uint32_t c = static_cast<uint32_t>((lane & 7) ^ swz_rope(R));
+      dma16(rd, dst + LAT_BYTES + wave * 1024,
+            static_cast<uint32_t>(r.rope[half]) * rope_rb + c * 16, 0);
+    }
   };
+  {
+    const Rows r0 = rows_of(0);
 #pragma unroll
-  for (int k = 0; k < 2 * A4_STEPS; k++) stage(0, k, true);
+    for (int k = 0; k < 2 * A4_STEPS; k++) stage(0, k, true, r0);
+  }
 
   // L2 prefetch of iteration it: wave w touches the 9 lines (8 latent, 1
   // rotary) of rows [16w, 16w + 16) of that iteration with A4_PF_LOADS
@@ -738,11 +780,10 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
   // loads have long completed.
   const uint16_t* lat_b = static_cast<const uint16_t*>(p.latent) + static_cast<int64_t>(b) * p.lat_bs;
   const uint16_t* rope_b = static_cast<const uint16_t*>(p.rope) + static_cast<int64_t>(b) * p.rope_bs;
-  auto prefetch = [&](int it, int k) -> uint32_t {
+  auto prefetch = [&](int k, const Rows& r) -> uint32_t {
     const int L = 64 * k + lane;
-    const int rr = min(L / 9, 15), ln = L - (L / 9) * 9;
-    int row = min(row_begin + it * 2 * TILE + 16 * wave + rr, row_end - 1);
-    row = idx_lds[row - row_begin];
+    const int ln = L - (L / 9) * 9;
+    const int row = r.pf[k];
     const uint16_t* a = ln < 8 ? lat_b + static_cast<int64_t>(row) * p.lat_rs + 64 * ln
                                : rope_b + static_cast<int64_t>(row) * p.rope_rs;
     return *reinterpret_cast<const uint32_t*>(a);
@@ -774,8 +815,11 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
 #pragma unroll
     for (int j = 0; j < D_R / 16; j++) q[D_C / 16 + j] = as_bf16x8(ld16(qp + 16 * j));
   }
+  {
+    const Rows r1 = rows_of(1);
 #pragma unroll
-  for (int k = 0; k < A4_PF_LOADS; k++) pf_pend[k] = prefetch(1, k);
+    for (int k = 0; k < A4_PF_LOADS; k++) pf_pend[k] = prefetch(k, r1);
+  }
   uint32_t sink = 0u;
 
   // per-lane LDS byte offsets inside a 32-row half (tile-independent)
@@ -820,8 +864,17 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
     // L2 prefetch of the one after are issued between the first multiplies.
     // Lanes of heads past n_h compute on clamped heads (every wave runs the
     // same code; nothing of theirs is stored). ----
-    floatx16 S = {};
+    // row indices of the next iteration's staging and of the prefetch after
+    // it, before the first tile operand read
+    const Rows rs = rows_of(it + 1);
+    const Rows rp = rows_of(it + 2);
+    floatx16 S;
     {
+      // two accumulators (even and odd k-steps): consecutive multiplies are
+      // independent, so the chain is not held to the latency of a multiply
+      // that waits for the previous result (one wave per SIMD: nothing else
+      // would fill the gap)
+      floatx16 S2[2] = {floatx16{}, floatx16{}};
       auto operand = [&](int j) -> u32x4 {
         if (j < D_C / 16) return *reinterpret_cast<const u32x4*>(half + s_off + 32 * j);
         return *reinterpret_cast<const u32x4*>(half + r_off +
@@ -834,11 +887,16 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
       for (int j = 0; j < NKS; j++) {
         const u32x4 a = ring[j % A4_SRING];
         if (j + A4_SRING < NKS) ring[j % A4_SRING] = operand(j + A4_SRING);
-        if (j < 2 * A4_STEPS) stage(it + 1, j, next);
+        if (j < 2 * A4_STEPS) stage(it + 1, j, next, rs);
         if (j >= 2 * A4_STEPS && j < 2 * A4_STEPS + A4_PF_LOADS)
-          pf_pend[j - 2 * A4_STEPS] = prefetch(it + 2, j - 2 * A4_STEPS);
-        S = mfma32x32x16(as_bf16x8(a), q[j], S);
+          pf_pend[j - 2 * A4_STEPS] = prefetch(j - 2 * A4_STEPS, rp);
+        S2[j & 1] = mfma32x32x16(as_bf16x8(a), q[j], S2[j & 1]);
+        // keep each read-ahead with its multiply: the scheduler would
+        // otherwise sink the reads next to their use and expose the LDS
+        // latency on every k-step
+        __builtin_amdgcn_sched_barrier(0);
       }
+      S = S2[0] + S2[1];
     }
     // ---- this half's visible rows and its maximum ----
     {
@@ -905,32 +963,37 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
         const char* mp = buf + hh * A4_HALF + m_off + 8704 * kk + 64 * fb;
         return tr_pair(mp, mp + 4368);
       };
+      // sub-step st = (block pair fp = st / 2, row half hh = st % 2): the four
+      // multiplies (block 2fp, 2fp+1) x (k-step 0, 1) alternate between the
+      // two blocks, so no multiply waits for the one just before it; the
+      // operands of the next sub-step are read meanwhile
       auto mix = [&](auto rescale) {
-        bf16x8 A[A4_MRING][4];
+        auto load4 = [&](int st, bf16x8 (&A)[4]) {
+          const int fp = st >> 1, hh = st & 1;
 #pragma unroll
-        for (int j = 0; j < A4_MRING; j++)
+          for (int c = 0; c < 4; c++) A[c] = mixop(2 * fp + (c & 1), hh, c >> 1);
+        };
+        bf16x8 A[2][4];
+        load4(0, A[0]);
 #pragma unroll
-          for (int c = 0; c < 4; c++) A[j][c] = mixop(j, c >> 1, c & 1);
+        for (int st = 0; st < 2 * NFB / 2; st++) {
+          const int fp = st >> 1, hh = st & 1;
+          if (st + 1 < NFB) load4(st + 1, A[(st + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (decltype(rescale)::value && hh == 0) {
 #pragma unroll
-        for (int fb = 0; fb < NFB; fb++) {
-          bf16x8 a[4];
-#pragma unroll
-          for (int c = 0; c < 4; c++) a[c] = A[fb % A4_MRING][c];
-          if (fb + A4_MRING < NFB) {
-#pragma unroll
-            for (int c = 0; c < 4; c++)
-              A[fb % A4_MRING][c] = mixop(fb + A4_MRING, c >> 1, c & 1);
-          }
-          if (decltype(rescale)::value) {
-            floatx16 t = O[fb] * f;
-            // back into accumulation registers, so that the multiplies below
-            // (and so both copies of the loop) keep O in the same registers
-            asm volatile("" : "+a"(t));
-            O[fb] = t;
+            for (int i = 0; i < 2; i++) {
+              floatx16 t = O[2 * fp + i] * f;
+              // back into accumulation registers, so that the multiplies
+              // (and so both copies of the loop) keep O in the same registers
+              asm volatile("" : "+a"(t));
+              O[2 * fp + i] = t;
+            }
           }
 #pragma unroll
           for (int c = 0; c < 4; c++)
-            O[fb] = mfma32x32x16(a[c], as_bf16x8(P[c >> 1][c & 1]), O[fb]);
+            O[2 * fp + (c & 1)] =
+                mfma32x32x16(A[st & 1][c], as_bf16x8(P[hh][c >> 1]), O[2 * fp + (c & 1)]);
         }
       };
       if (rescaled)

@@ -127,14 +127,23 @@ def test_decode_step_one_call(B, S_q, n_h, T, dtype, causal, topk):
     check(f64(lse), ref_lse, TOL[dtype], "lse")
 
 
-def test_decode_step_single_token_equals_the_three_calls():
-    inp = synth.config_inputs(2)
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_decode_step_single_token_equals_the_three_calls(cfg):
+    # the benchmark's one-call step (packed queries, split merge fused into
+    # W^UV) against the separate calls the parity tests check against the
+    # oracle, at the full workload sizes: the same bits
+    print(f"step vs three calls: config {cfg}", flush=True)
+    inp = synth.config_inputs(cfg)
     d = {k: v.to(DEV) for k, v in inp.items()}
+    if cfg == 4:
+        d["wkv_b"] = mla.mla_dequant_fp8_block(d["wkv_b_fp8"], d["wkv_b_scale"])
+    idx = d.get("topk_idx")
     cache = d["cache"]
     one = mla.mla_decode_step(d["q_nope"], d["q_pe"], d["wkv_b"], cache[..., :512],
-                              cache[..., 512:])
+                              cache[..., 512:], topk_idx=idx)
     q_lat = mla.mla_absorb_q(d["q_nope"], d["wkv_b"])
-    o_lat = mla.mla_decode_latent_attn(q_lat, d["q_pe"], cache[..., :512], cache[..., 512:])
+    o_lat = mla.mla_decode_latent_attn(q_lat, d["q_pe"], cache[..., :512], cache[..., 512:],
+                                       topk_idx=idx)
     three = mla.mla_out_up(o_lat, d["wkv_b"])
     torch.cuda.synchronize()
     assert torch.equal(one.cpu().view(torch.int16), three.cpu().view(torch.int16))
