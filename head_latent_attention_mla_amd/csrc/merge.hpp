@@ -11,14 +11,54 @@ namespace mla {
 
 constexpr int MERGE_CHUNK = 8;  // splits per memory round trip
 
+// One chunk of MERGE_CHUNK splits (s0 .. s0+7; log-sum-exps lv, partials v:
+// 8 consecutive bf16 features) folded into the running state (mx, wsum,
+// acc) of one row: the running maximum absorbs the chunk's, state and new
+// terms are weighted by exp(lse - max). Entries past the last split (their
+// indices were clamped by the caller) weigh zero; while no split has seen a
+// position (cm = -inf: every index outside [0, T)) nothing is added.
+__device__ __forceinline__ void merge_fold8(const float (&lv)[MERGE_CHUNK],
+                                            const u32x4 (&v)[MERGE_CHUNK], int s0, int S,
+                                            float& mx, float& wsum, float (&acc)[8]) {
+  float cm = mx;
+#pragma unroll
+  for (int j = 0; j < MERGE_CHUNK; j++) cm = fmaxf(cm, lv[j]);
+  // f is 0 on the first chunk (mx = -inf)
+  const float f = cm != -INFINITY ? __expf(mx - cm) : 1.f;
+  wsum *= f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc[i] *= f;
+  mx = cm;
+#pragma unroll
+  for (int j = 0; j < MERGE_CHUNK; j++) {
+    const float w = s0 + j < S && cm != -INFINITY ? __expf(lv[j] - mx) : 0.f;
+    wsum += w;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      acc[2 * i] = fmaf(w, __uint_as_float(v[j][i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w, __uint_as_float(v[j][i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+  }
+}
+
+// The merged values (fp32, before rounding) and the row's log-sum-exp from
+// the state after the last chunk; a row whose splits all saw no position
+// merges to zero with lse -inf (the empty sum).
+__device__ __forceinline__ float merge_finish(float mx, float wsum, const float (&acc)[8],
+                                              float (&out)[8]) {
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = acc[i] * inv;
+  return mx + logf(wsum);
+}
+
 // 8 consecutive latent features (c0..c0+7) of NR query rows bh[0..NR-1]:
 // partials are [S][BH][512] bf16, lse [S][BH] fp32. Splits are taken
 // MERGE_CHUNK at a time; a chunk's log-sum-exps and partials of all NR rows
-// are loaded together (one memory round trip per chunk; indices past the
-// last split are clamped and weighted zero) and folded in with a running
-// maximum. Returns the merged values (fp32, before rounding) and each row's
-// log-sum-exp; a row whose splits all saw no position (lse -inf) merges to
-// zero with lse -inf. The arithmetic of a row does not depend on NR.
+// are loaded together (one memory round trip per chunk, or for one row of 9
+// to 16 splits both chunks in one round trip; indices past the last split
+// are clamped) and folded in with merge_fold8. The arithmetic of a row does
+// not depend on NR or on how its chunks were loaded.
 template <int NR>
 __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
                                             const float* __restrict__ ws_lse, int S, int64_t BH,
@@ -32,48 +72,34 @@ __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[r][i] = 0.f;
   }
-  for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
-    u32x4 v[NR][MERGE_CHUNK];
-    float lv[NR][MERGE_CHUNK];
+  auto load = [&](int r, int s0, float (&lv)[MERGE_CHUNK], u32x4 (&v)[MERGE_CHUNK]) {
 #pragma unroll
-    for (int r = 0; r < NR; r++)
+    for (int j = 0; j < MERGE_CHUNK; j++) {
+      const int64_t sj = min(s0 + j, S - 1);
+      lv[j] = ws_lse[sj * BH + bh[r]];
+      v[j] = ld16(ws_o + (sj * BH + bh[r]) * D_C + c0);
+    }
+  };
+  if (NR == 1 && S > MERGE_CHUNK && S <= 2 * MERGE_CHUNK) {
+    // two chunks of one row: both in one memory round trip
+    u32x4 v0[MERGE_CHUNK], v1[MERGE_CHUNK];
+    float l0[MERGE_CHUNK], l1[MERGE_CHUNK];
+    load(0, 0, l0, v0);
+    load(0, MERGE_CHUNK, l1, v1);
+    merge_fold8(l0, v0, 0, S, mx[0], wsum[0], acc[0]);
+    merge_fold8(l1, v1, MERGE_CHUNK, S, mx[0], wsum[0], acc[0]);
+  } else {
+    for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
+      u32x4 v[NR][MERGE_CHUNK];
+      float lv[NR][MERGE_CHUNK];
 #pragma unroll
-      for (int j = 0; j < MERGE_CHUNK; j++) {
-        const int64_t sj = min(s0 + j, S - 1);
-        lv[r][j] = ws_lse[sj * BH + bh[r]];
-        v[r][j] = ld16(ws_o + (sj * BH + bh[r]) * D_C + c0);
-      }
+      for (int r = 0; r < NR; r++) load(r, s0, lv[r], v[r]);
 #pragma unroll
-    for (int r = 0; r < NR; r++) {
-      float cm = mx[r];
-#pragma unroll
-      for (int j = 0; j < MERGE_CHUNK; j++) cm = fmaxf(cm, lv[r][j]);
-      // f is 0 on the first chunk (mx = -inf); while no split has seen a
-      // position (cm = -inf: every index outside [0, T)) nothing is added
-      const float f = cm != -INFINITY ? __expf(mx[r] - cm) : 1.f;
-      wsum[r] *= f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) acc[r][i] *= f;
-      mx[r] = cm;
-#pragma unroll
-      for (int j = 0; j < MERGE_CHUNK; j++) {
-        const float w = s0 + j < S && cm != -INFINITY ? __expf(lv[r][j] - mx[r]) : 0.f;
-        wsum[r] += w;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          acc[r][2 * i] = fmaf(w, __uint_as_float(v[r][j][i] << 16), acc[r][2 * i]);
-          acc[r][2 * i + 1] = fmaf(w, __uint_as_float(v[r][j][i] & 0xFFFF0000u), acc[r][2 * i + 1]);
-        }
-      }
+      for (int r = 0; r < NR; r++) merge_fold8(lv[r], v[r], s0, S, mx[r], wsum[r], acc[r]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < NR; r++) {
-    const float inv = wsum[r] > 0.f ? 1.f / wsum[r] : 0.f;  // the empty sum is 0
-#pragma unroll
-    for (int i = 0; i < 8; i++) out[r][i] = acc[r][i] * inv;
-    lse[r] = mx[r] + logf(wsum[r]);
-  }
+  for (int r = 0; r < NR; r++) lse[r] = merge_finish(mx[r], wsum[r], acc[r], out[r]);
 }
 
 }  // namespace mla
