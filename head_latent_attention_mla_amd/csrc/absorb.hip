@@ -15,11 +15,14 @@
 // quarter and computes the transposed product
 //   q_lat^T[32 columns x 32 rows] = W^T[columns x d] . q_nope^T[d x rows]
 // (8 k-steps of v_mfma_f32_32x32x16_bf16 per 32-row batch tile; A = W^T from
-// LDS, held in registers across batch tiles; B = 16-byte loads of q_nope
-// rows). The column order tau makes accumulator r of lane half g column
-// 16g + r, so every lane stores 32 contiguous bytes. LDS rows are
-// XOR-swizzled by 4 * (row mod 4) chunks, which keeps the transposing reads
-// free of bank conflicts.
+// LDS, held in registers across batch tiles; B = the batch tile's q_nope
+// rows, staged once per workgroup into LDS by LDS-DMA (the four waves read
+// the same rows: staged once, the workgroup fetches 8 KB per tile instead of
+// 32 KB), double-buffered across batch tiles). The column order tau makes
+// accumulator r of lane half g column 16g + r, so every lane stores 32
+// contiguous bytes. LDS rows of W are XOR-swizzled by 4 * (row mod 4)
+// chunks, rows of q_nope by (row mod 16) chunks, which keeps both kinds of
+// reads free of bank conflicts.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -56,6 +59,7 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ q_lat, int B,
                                                             int n_h, int swz_sq) {
   __shared__ __attribute__((aligned(16))) char wl[AB_BYTES];
+  __shared__ __attribute__((aligned(16))) char qt[2][32 * D_N * 2];  // q_nope batch tiles
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
@@ -82,16 +86,24 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
       dma16(rs, dst + (wave + 4 * j) * 1024, static_cast<uint32_t>(r * D_C * 2 + c * 16), 0);
     }
   }
-  // q_nope rows of the first batch tile (rows past B re-read row B-1)
+  // q_nope rows of batch tile bt into qt[bt & 1] (rows past B re-read row
+  // B-1): LDS chunk p of row r holds the row's 16-byte chunk p ^ (r mod 16);
+  // 1 KB block j = wave + 4k, k = 0, 1, of the 8 KB tile per DMA
   const int nbt = (B + 31) >> 5;
-  auto load_q = [&](int bt, u32x4* qv) {
-    const int b = min(bt * 32 + n, B - 1);
-    const uint16_t* qrow = q_nope + (static_cast<int64_t>(b) * n_h + h) * D_N + 8 * g;
+  const uint32_t qt_addr = __builtin_amdgcn_readfirstlane(lds_addr(qt));
+  auto stage_q = [&](int bt) {
+    const i32x4 rs = make_rsrc(q_nope + (static_cast<int64_t>(bt) * 32 * n_h + h) * D_N);
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++) qv[ks] = ld16(qrow + 16 * ks);
+    for (int k = 0; k < 2; k++) {
+      const int j = wave + 4 * k;
+      const int pch = j * 64 + lane;
+      const int r = pch >> 4, c = (pch & 15) ^ (r & 15);
+      const int rr = min(bt * 32 + r, B - 1) - bt * 32;  // row within the tile's base
+      dma16(rs, qt_addr + (bt & 1) * (32 * D_N * 2) + j * 1024,
+            static_cast<uint32_t>(rr * n_h * (D_N * 2) + c * 16), 0);
+    }
   };
-  u32x4 qv[8];
-  load_q(0, qv);
+  stage_q(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -112,16 +124,18 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
   }
   const int col = cq * 128 + 32 * wave + 16 * g;  // first of this lane's 16 output columns
   for (int bt = 0; bt < nbt; bt++) {
-    // next tile's rows into a second register set, issued before the
-    // multiplies: no branch between the multiplies and the reads of their
-    // accumulators
-    u32x4 qn[8];
-    if (bt + 1 < nbt) load_q(bt + 1, qn);
+    // the next tile's rows are staged into the other buffer (free: every
+    // wave passed the barrier after reading it) while this one multiplies
+    if (bt + 1 < nbt) stage_q(bt + 1);
+    u32x4 qv[8];
+    {
+      const char* qrow = qt[bt & 1] + n * (D_N * 2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ks++) qv[ks] = ld_lds16(qrow + 16 * ((2 * ks + g) ^ (n & 15)));
+    }
     floatx16 acc = floatx16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) acc = mfma32x32x16(A[ks], as_bf16x8(qv[ks]), acc);
-#pragma unroll
-    for (int ks = 0; ks < 8; ks++) qv[ks] = qn[ks];
     const int b = bt * 32 + n;
     if (b < B) {
       u32x4 v0, v1;
@@ -144,6 +158,11 @@ __global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __re
         st16(dst, v0);
         st16(dst + 32 * 8, v1);
       }
+    }
+    if (bt + 1 < nbt) {
+      // the next tile landed (the wait also covers this tile's stores)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
   }
 }
