@@ -105,13 +105,19 @@ __global__ __launch_bounds__(256) void out_up_bf16_kernel(const uint16_t* __rest
 // merge + out-up. The MFMA tile has 32 rows: rows 16..31 repeat 0..15 and
 // are not stored. LDS rows are XOR-swizzled by (row mod 16) chunks so the
 // 16 rows of an operand read hit distinct banks.
+// With NV = 2 (a batch of at most 16 rows and fewer than 256 (head, tile)
+// workgroups) the value features are split between two workgroups, so the
+// whole chip streams W^UV and the partials (the second workgroup's partial
+// rows come from L2): wave (dt, kq) then multiplies one 128-feature quarter
+// kq for value block dt, and the quarter sums meet in LDS in the same order.
 constexpr int MO_ROWS = 16;
+template <int NV>
 __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
     const uint16_t* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
     const uint16_t* __restrict__ w, uint16_t* __restrict__ out, float* __restrict__ lse, int B,
     int n_h) {
   __shared__ __attribute__((aligned(16))) char ol[MO_ROWS * D_C * 2];   // merged rows
-  __shared__ __attribute__((aligned(16))) floatx4 red[2][4][2][64];     // kh = 1 quarter sums
+  __shared__ __attribute__((aligned(16))) floatx4 red[16][64];  // quarter sums of the other waves
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
@@ -120,18 +126,23 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
   int L = blockIdx.x;
   const int G = gridDim.x;
   if ((n_h & 7) == 0) L = (L >> 3) + (L & 7) * (G >> 3);
-  const int bt = L % nbt;
-  const int hh = L / nbt;
+  const int vp = L % NV;  // value part (the parts of a (head, tile) are adjacent)
+  const int bt = (L / NV) % nbt;
+  const int hh = L / (NV * nbt);
   const int h = (n_h & 7) == 0 ? (hh % (n_h >> 3)) * 8 + hh / (n_h >> 3) : hh;
-  const int dt = wave & 3, kh = wave >> 2;
+  // NV = 1: wave (dt, kh) takes quarters 2kh, 2kh+1; NV = 2: wave (dt, kq)
+  // quarter kq, value blocks 2vp, 2vp+1
+  constexpr int NQ = 2 / NV;               // quarters per wave
+  const int dt = NV == 1 ? (wave & 3) : 2 * vp + (wave & 1);
+  const int q0 = NV == 1 ? 2 * (wave >> 2) : (wave >> 1);  // first quarter of this wave
   const int d = dt * 32 + n;
 
-  u32x4 bw[16];
+  u32x4 bw[8 * NQ];
   {
     const uint16_t* wrow =
-        w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C + kh * 256 + g * 8;
+        w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + D_N + d) * D_C + q0 * 128 + g * 8;
 #pragma unroll
-    for (int k = 0; k < 16; k++) bw[k] = ld16(wrow + 16 * k);
+    for (int k = 0; k < 8 * NQ; k++) bw[k] = ld16(wrow + 16 * k);
   }
   const int64_t BH = static_cast<int64_t>(B) * n_h;
   {
@@ -162,38 +173,48 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
     }
   }
   __syncthreads();
-  // two 128-feature quarters per wave, summed in the order the stand-alone
-  // W^UV kernel uses ((q0 + q1) + q2) + q3, so both paths give the same bits
-  floatx16 acc[2] = {floatx16{}, floatx16{}};
+  // each quarter is one 8-k-step chain from zero; the quarters are summed in
+  // the order the stand-alone W^UV kernel uses ((q0 + q1) + q2) + q3, so
+  // both paths give the same bits
+  floatx16 acc[NQ];
+#pragma unroll
+  for (int qq = 0; qq < NQ; qq++) acc[qq] = floatx16{};
   {
     const int r = n & 15;
     const char* arow = ol + r * (D_C * 2);
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
-      const int c = kh * 32 + 2 * k + g;
+    for (int k = 0; k < 8 * NQ; k++) {
+      const int c = q0 * 16 + 2 * k + g;
       const u32x4 a = ld_lds16(arow + 16 * (c ^ r));
       acc[k >> 3] = mfma32x32x16(as_bf16x8(a), as_bf16x8(bw[k]), acc[k >> 3]);
     }
   }
-  // accumulators 0..7 of lane half g hold rows 8*(r/4) + 4g + r%4 < 16
-  if (kh == 1) {
+  // accumulators 0..7 of lane half g hold rows 8*(r/4) + 4g + r%4 < 16;
+  // the quarters the first waves (those holding quarter 0) do not hold meet
+  // in red: NV = 1 quarters 2, 3 of value block dt; NV = 2 quarters 1..3 of
+  // block dt & 1 (two float4 per lane each)
+  auto slot = [&](int q, int q4) {
+    return NV == 1 ? ((q - 2) * 4 + dt) * 2 + q4 : ((q - 1) * 2 + (dt & 1)) * 2 + q4;
+  };
+  const bool first = q0 == 0;
+  if (!first) {
 #pragma unroll
-    for (int qq = 0; qq < 2; qq++)
+    for (int qq = 0; qq < NQ; qq++)
 #pragma unroll
       for (int q4 = 0; q4 < 2; q4++)
-        red[qq][dt][q4][lane] = floatx4{acc[qq][4 * q4], acc[qq][4 * q4 + 1],
-                                        acc[qq][4 * q4 + 2], acc[qq][4 * q4 + 3]};
+        red[slot(q0 + qq, q4)][lane] = floatx4{acc[qq][4 * q4], acc[qq][4 * q4 + 1],
+                                                     acc[qq][4 * q4 + 2], acc[qq][4 * q4 + 3]};
   }
   __syncthreads();
-  if (kh == 0) {
+  if (first) {
     float sum[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) sum[i] = acc[0][i] + acc[1][i];
+    for (int i = 0; i < 8; i++) sum[i] = NQ == 2 ? acc[0][i] + acc[NQ - 1][i] : acc[0][i];
 #pragma unroll
-    for (int qq = 0; qq < 2; qq++)
+    for (int q = NQ; q < 4; q++)
 #pragma unroll
       for (int q4 = 0; q4 < 2; q4++) {
-        const floatx4 v = red[qq][dt][q4][lane];
+        const floatx4 v = red[slot(q, q4)][lane];
         sum[4 * q4] += v[0];
         sum[4 * q4 + 1] += v[1];
         sum[4 * q4 + 2] += v[2];
@@ -209,11 +230,17 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
 
 hipError_t launch_merge_out_up(const void* ws_o, const float* ws_lse, int S, const void* wkv_b,
                                void* out, float* lse, int B, int n_h, hipStream_t stream) {
-  const int blocks = n_h * ((B + MO_ROWS - 1) / MO_ROWS);
-  hipLaunchKernelGGL(merge_out_up_bf16_kernel, dim3(blocks), dim3(512), 0, stream,
-                     static_cast<const uint16_t*>(ws_o), ws_lse, S,
-                     static_cast<const uint16_t*>(wkv_b), static_cast<uint16_t*>(out), lse, B,
-                     n_h);
+  const int tiles = n_h * ((B + MO_ROWS - 1) / MO_ROWS);
+  if (tiles < 256 && (n_h & 7) == 0)
+    hipLaunchKernelGGL(merge_out_up_bf16_kernel<2>, dim3(2 * tiles), dim3(512), 0, stream,
+                       static_cast<const uint16_t*>(ws_o), ws_lse, S,
+                       static_cast<const uint16_t*>(wkv_b), static_cast<uint16_t*>(out), lse, B,
+                       n_h);
+  else
+    hipLaunchKernelGGL(merge_out_up_bf16_kernel<1>, dim3(tiles), dim3(512), 0, stream,
+                       static_cast<const uint16_t*>(ws_o), ws_lse, S,
+                       static_cast<const uint16_t*>(wkv_b), static_cast<uint16_t*>(out), lse, B,
+                       n_h);
   return hipGetLastError();
 }
 
