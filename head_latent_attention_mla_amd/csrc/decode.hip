@@ -680,15 +680,43 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
   const uint32_t rope_rb = static_cast<uint32_t>(p.rope_rs * 2);
   const uint32_t tiles_addr = __builtin_amdgcn_readfirstlane(lds_addr(tiles));
 
+  // queries of this lane's head (loaded below, with the index entries)
+  const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
+  bf16x8 q[D_QK / 16];
   {
     // The index set is a scatter into a -inf row: an entry outside [0, T)
     // addresses no position. Such entries are staged as row 0 (so every
     // fetch stays inside the cache) and cleared in vmask (weight zero).
     const int* src = p.idx + static_cast<int64_t>(b) * p.K + row_begin;
     const int n_rows = row_end - row_begin;
+    // the first chunk of entries, then the queries: the query loads stay in
+    // flight while the entries are checked and published, so their latency
+    // overlaps the round trip of the entries
+    const int v_first = static_cast<int>(threadIdx.x) < n_rows ? src[threadIdx.x] : -1;
+    // queries of this lane's head: 32 latent k-steps (rows layout: features
+    // 16ks + 8g of the row; operand order: one contiguous KiB per k-step and
+    // 32-head block) and the 4 rotary k-steps
+    {
+      const uint16_t* ql;
+      int step;
+      if (p.q_swz) {
+        ql = static_cast<const uint16_t*>(p.q_lat) +
+             ((static_cast<int64_t>(b) * (p.n_h >> 7) + (hblk >> 2)) * 4 + (hblk & 3)) * (32 * 512) +
+             8 * lane;
+        step = 512;
+      } else {
+        ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
+        step = 16;
+      }
+#pragma unroll
+      for (int j = 0; j < D_C / 16; j++) q[j] = as_bf16x8(ld16(ql + step * j));
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R + 8 * g;
+#pragma unroll
+      for (int j = 0; j < D_R / 16; j++) q[D_C / 16 + j] = as_bf16x8(ld16(qp + 16 * j));
+    }
     for (int i0 = 0; i0 < n_rows; i0 += A4_WAVES * 64) {
       const int i = i0 + threadIdx.x;
-      const int v = i < n_rows ? src[i] : -1;
+      const int v = i0 == 0 ? v_first : (i < n_rows ? src[i] : -1);
       const bool ok = v >= 0 && v < p.T;
       if (i < n_rows) idx_lds[i] = ok ? v : 0;
       const uint64_t bal = __ballot(ok);
@@ -792,29 +820,6 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
 #pragma unroll
   for (int k = 0; k < A4_PF_LOADS; k++) pf_old[k] = 0u;
 
-  // queries of this lane's head: 32 latent k-steps (rows layout: features
-  // 16ks + 8g of the row; operand order: one contiguous KiB per k-step and
-  // 32-head block) and the 4 rotary k-steps
-  const int64_t qrow = static_cast<int64_t>(b) * p.n_h + headc;
-  bf16x8 q[D_QK / 16];
-  {
-    const uint16_t* ql;
-    int step;
-    if (p.q_swz) {
-      ql = static_cast<const uint16_t*>(p.q_lat) +
-           ((static_cast<int64_t>(b) * (p.n_h >> 7) + (hblk >> 2)) * 4 + (hblk & 3)) * (32 * 512) +
-           8 * lane;
-      step = 512;
-    } else {
-      ql = static_cast<const uint16_t*>(p.q_lat) + qrow * D_C + 8 * g;
-      step = 16;
-    }
-#pragma unroll
-    for (int j = 0; j < D_C / 16; j++) q[j] = as_bf16x8(ld16(ql + step * j));
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + qrow * D_R + 8 * g;
-#pragma unroll
-    for (int j = 0; j < D_R / 16; j++) q[D_C / 16 + j] = as_bf16x8(ld16(qp + 16 * j));
-  }
   {
     const Rows r1 = rows_of(1);
 #pragma unroll
