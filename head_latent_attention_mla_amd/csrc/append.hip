@@ -93,39 +93,44 @@ __global__ __launch_bounds__(64 * APPEND_WAVES) void cache_append_kernel(AppendP
   const int64_t n0 =
       (static_cast<int64_t>(blockIdx.x) * APPEND_WAVES + (threadIdx.x >> 6)) * ROWS;
   const int esz = BF16 ? 2 : 4;
-  float x[ROWS][8], k4[ROWS][4];
+  // loads in two rounds: (1) the row indices, the rows themselves and the
+  // gains (none depends on another); (2) the rotation-table rows, which need
+  // the positions. The loaded vectors are kept raw until both rounds are out.
+  u32x4 raw[ROWS][2];  // bf16: raw[r][0] = 8 latent features; fp32: [0], [1] = two halves
+  u32x4 kraw[ROWS];    // rotary key: bf16 4 features in .x/.y; fp32 4 floats
   floatx4 cs[ROWS];
   int64_t dst_lat[ROWS], dst_rope[ROWS];
   bool ok[ROWS];
+  int tpos[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const int64_t n = n0 + r;
     const bool in = n < p.N;
     const int s = !in ? -1 : (p.seq_idx ? p.seq_idx[n] : static_cast<int>(n));
     const int t = in ? p.pos[n] : -1;
+    tpos[r] = t;
     // rows addressed outside the cache or the rotation table are not written
     ok[r] = in && s >= 0 && s < p.B_cache && t >= 0 && t < p.T_cache && t < p.n_pos;
     dst_lat[r] = s * p.lat_bs + t * p.lat_rs;
     dst_rope[r] = s * p.rope_bs + t * p.rope_rs;
-    if (ok[r]) {
-      const char* src = static_cast<const char*>(p.kv_a) + n * p.in_rstride * esz;
-      load_lat<BF16>(src, lane, x[r]);
-      if (lane < D_R / 4) {  // 16 lanes x 4 rotary features (2 pairs)
-        if constexpr (BF16) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(
-              reinterpret_cast<const uint16_t*>(src) + D_C + 4 * lane);
-          k4[r][0] = __uint_as_float(v[0] << 16);
-          k4[r][1] = __uint_as_float(v[0] & 0xFFFF0000u);
-          k4[r][2] = __uint_as_float(v[1] << 16);
-          k4[r][3] = __uint_as_float(v[1] & 0xFFFF0000u);
-        } else {
-          const floatx4 v = *reinterpret_cast<const floatx4*>(
-              reinterpret_cast<const float*>(src) + D_C + 4 * lane);
-          for (int k = 0; k < 4; ++k) k4[r][k] = v[k];
-        }
-        // (cos, sin) of pairs 2*lane and 2*lane + 1
-        cs[r] = *reinterpret_cast<const floatx4*>(p.freqs + static_cast<int64_t>(t) * D_R +
-                                                  4 * lane);
+    // the row itself depends only on n: its loads go out with the index loads
+    const int64_t nn = in ? n : 0;
+    const char* src = static_cast<const char*>(p.kv_a) + nn * p.in_rstride * esz;
+    if constexpr (BF16) {
+      raw[r][0] = ld16(static_cast<const uint16_t*>(static_cast<const void*>(src)) + 8 * lane);
+      raw[r][1] = raw[r][0];
+    } else {
+      raw[r][0] = ld16(reinterpret_cast<const float*>(src) + 4 * lane);
+      raw[r][1] = ld16(reinterpret_cast<const float*>(src) + 256 + 4 * lane);
+    }
+    kraw[r] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < D_R / 4) {  // 16 lanes x 4 rotary features (2 pairs)
+      if constexpr (BF16) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(
+            reinterpret_cast<const uint16_t*>(src) + D_C + 4 * lane);
+        kraw[r] = u32x4{v[0], v[1], 0u, 0u};
+      } else {
+        kraw[r] = ld16(reinterpret_cast<const float*>(src) + D_C + 4 * lane);
       }
     }
   }
@@ -134,19 +139,50 @@ __global__ __launch_bounds__(64 * APPEND_WAVES) void cache_append_kernel(AppendP
   for (int k = 0; k < 8; ++k) g[k] = p.gamma[lat_feature<BF16>(lane, k)];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
+    // (cos, sin) of pairs 2*lane and 2*lane + 1
+    cs[r] = floatx4{1.f, 0.f, 1.f, 0.f};
+    if (ok[r] && lane < D_R / 4)
+      cs[r] = *reinterpret_cast<const floatx4*>(p.freqs + static_cast<int64_t>(tpos[r]) * D_R +
+                                                4 * lane);
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
     if (!ok[r]) continue;
+    float x[8];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(raw[r][0][k] << 16);
+        x[2 * k + 1] = __uint_as_float(raw[r][0][k] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] = __uint_as_float(raw[r][0][k]);
+        x[4 + k] = __uint_as_float(raw[r][1][k]);
+      }
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ss += x[r][k] * x[r][k];
+    for (int k = 0; k < 8; ++k) ss += x[k] * x[k];
     ss = wave_sum(ss);
     // 1/512 is a power of two: the mean is exact in fp32
     const float inv = rsqrtf(ss * (1.0f / D_C) + p.eps);
     float y[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = g[k] * (x[r][k] * inv);
+    for (int k = 0; k < 8; ++k) y[k] = g[k] * (x[k] * inv);
     store_lat<BF16>(static_cast<char*>(p.latent) + dst_lat[r] * esz, lane, y);
     if (lane < D_R / 4) {
-      const float* kk = k4[r];
+      float kk[4];
+      if constexpr (BF16) {
+        kk[0] = __uint_as_float(kraw[r][0] << 16);
+        kk[1] = __uint_as_float(kraw[r][0] & 0xFFFF0000u);
+        kk[2] = __uint_as_float(kraw[r][1] << 16);
+        kk[3] = __uint_as_float(kraw[r][1] & 0xFFFF0000u);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kk[k] = __uint_as_float(kraw[r][k]);
+      }
       const floatx4 c = cs[r];
       const float o0 = kk[0] * c[0] - kk[1] * c[1];
       const float o1 = kk[0] * c[1] + kk[1] * c[0];
