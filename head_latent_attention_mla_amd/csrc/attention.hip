@@ -74,6 +74,11 @@ constexpr int AT_DMA = AT_K_DMA + AT_V_DMA;        // + 1 mask DMA on waves 0, 1
 constexpr float AT_LOG2E = 1.4426950408889634f;
 constexpr float AT_LN2 = 0.6931471805599453f;
 constexpr float AT_SLACK = 8.0f;  // log2 units by which a score may exceed the running max
+#ifndef MLA_AT_AHEAD
+#define MLA_AT_AHEAD 6
+#endif
+constexpr int AT_SCORE_AHEAD = MLA_AT_AHEAD;  // key operands read ahead of the score multiplies
+constexpr int AT_MIX_AHEAD = MLA_AT_AHEAD;    // value operands read ahead of the mix multiplies
 
 static_assert(AT_K_BYTES % (1024 * AT_WAVES) == 0 && AT_V_BYTES % (1024 * AT_WAVES) == 0,
               "tiles must split into whole wave-DMAs");
@@ -242,20 +247,28 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
   const bool late = (wave & 1) != 0;
   bool pending = false;         // a late wave holds the weights of an unmixed tile
   u32x4 P[2][2];                // weights of the tile being mixed, bf16 [half][k-step]
-  // O^T += V^T . P^T over the 64 keys of the value tile at vbase
+  // O^T += V^T . P^T over the 64 keys of the value tile at vbase: 16
+  // multiplies, step j = (half, kk, mt), so consecutive multiplies update
+  // different accumulators; each accumulator still adds its four products in
+  // the order (half, kk). The transposing operand reads run AT_MIX_AHEAD
+  // steps ahead of their multiplies (an LDS round trip lasts several
+  // multiplies), each read kept with its multiply.
   auto mix = [&](const u32x4 (&Pm)[2][2], const char* vbase) {
+    auto operand = [&](int j) {
+      const int half = j >> 3, kk = (j >> 2) & 1, mt = j & 3;
+      const char* lo = vbase + 32 * half * AT_V_PITCH + v_off[mt] + 8 * kk * AT_V_PITCH;
+      return at_tr_pair(lo, lo + 4 * AT_V_PITCH);
+    };
+    bf16x8 ring[AT_MIX_AHEAD];
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
-      const char* vst = vbase + 32 * half * AT_V_PITCH;
+    for (int j = 0; j < AT_MIX_AHEAD; j++) ring[j] = operand(j);
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-          const char* lo = vst + v_off[mt] + 8 * kk * AT_V_PITCH;
-          const bf16x8 A = at_tr_pair(lo, lo + 4 * AT_V_PITCH);
-          o[mt] = mfma32x32x16(A, as_bf16x8(Pm[half][kk]), o[mt]);
-        }
-      }
+    for (int j = 0; j < 16; j++) {
+      const int half = j >> 3, kk = (j >> 2) & 1, mt = j & 3;
+      const bf16x8 A = ring[j % AT_MIX_AHEAD];
+      if (j + AT_MIX_AHEAD < 16) ring[j % AT_MIX_AHEAD] = operand(j + AT_MIX_AHEAD);
+      o[mt] = mfma32x32x16(A, as_bf16x8(Pm[half][kk]), o[mt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -282,14 +295,24 @@ __global__ __launch_bounds__(64 * AT_WAVES, 1) void attention_bf16_kernel(AttnPa
 
     // scores of both 32-key halves as two independent MFMA chains (a half
     // wholly past the wave's keys is computed and masked to weight 0)
+    // (key operands read AT_SCORE_AHEAD multiplies ahead, each read kept
+    // with its multiply)
     floatx16 s[2] = {floatx16{}, floatx16{}};
+    {
+      auto operand = [&](int j) {
+        const int ks = j >> 1, half = j & 1;
+        return ld_lds16(kst + 32 * half * AT_K_PITCH + k_off[ks & 3] + 128 * (ks >> 2));
+      };
+      u32x4 ring[AT_SCORE_AHEAD];
 #pragma unroll
-    for (int ks = 0; ks < 12; ks++) {
+      for (int j = 0; j < AT_SCORE_AHEAD; j++) ring[j] = operand(j);
 #pragma unroll
-      for (int half = 0; half < 2; half++) {
-        const bf16x8 A = as_bf16x8(
-            ld_lds16(kst + 32 * half * AT_K_PITCH + k_off[ks & 3] + 128 * (ks >> 2)));
-        s[half] = mfma32x32x16(A, as_bf16x8(qv[ks]), s[half]);
+      for (int j = 0; j < 24; j++) {
+        const int ks = j >> 1, half = j & 1;
+        const u32x4 A = ring[j % AT_SCORE_AHEAD];
+        if (j + AT_SCORE_AHEAD < 24) ring[j % AT_SCORE_AHEAD] = operand(j + AT_SCORE_AHEAD);
+        s[half] = mfma32x32x16(as_bf16x8(A), as_bf16x8(qv[ks]), s[half]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // mask: keys past T, past the query's position (causal), or outside the
