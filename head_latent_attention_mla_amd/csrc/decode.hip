@@ -483,8 +483,12 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_bf16_kernel(DecodeParam
       // SIMD's MFMA pipe meanwhile ----
       {
         const int valid = row_vis - (row_begin + it * TILE);  // visible rows of this tile
+        // (without the causal limit only a split's last tile can be partial:
+        // whole tiles skip the mask)
+        if (CAUSAL || valid < TILE) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
+          for (int r = 0; r < 16; r++) S[r] = 16 * g + r < valid ? S[r] : -INFINITY;
+        }
       }
       float smax = -INFINITY;
 #pragma unroll
