@@ -1015,7 +1015,13 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
   // the prefetched values are never needed; this keeps the loads (a sink
   // of all ones bits would need a cache of all-ones rows and a negative B)
   if (sink == 0xFFFFFFFFu && p.B < 0) p.lse[0] = 0.f;
-  // ---- epilogue: normalise and store features [256 ph, 256 ph + 256) ----
+  // ---- epilogue: normalise; the group's 64 partial rows are staged in LDS
+  // (the tile buffers are free once every wave is past the barrier below),
+  // so each store instruction writes whole 1 KB rows instead of 32 rows'
+  // 32-byte pieces. Row r of the stage is the group's head r: 64 chunks of
+  // 16 bytes, chunk c at position c ^ (r mod 64), which keeps the writes
+  // (32 rows, one chunk each) and the reads (one row, all chunks) free of
+  // bank conflicts. ----
   const float L = pair_sum(l);
   // a head with no visible row in this split: zero partial, lse -inf
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -1029,22 +1035,35 @@ __global__ __launch_bounds__(A4_WAVES * 64, 1) void attend64_bf16_kernel(DecodeP
       p.ws_lse[static_cast<int64_t>(s) * BH + bh] = lse_v;
     }
   }
-  if (head >= p.n_h) return;
+  __syncthreads();  // every wave is done with the tile buffers
+  {
+    const int row = hb * 32 + n;
+    char* const srow_p = tiles + row * (D_C * 2);
+#pragma unroll
+    for (int fb = 0; fb < NFB; fb++) {
+      u32x4 v0, v1;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; w2++) {
+        v0[w2] = pack_bf16x2(O[fb][2 * w2] * inv, O[fb][2 * w2 + 1] * inv);
+        v1[w2] = pack_bf16x2(O[fb][8 + 2 * w2] * inv, O[fb][8 + 2 * w2 + 1] * inv);
+      }
+      const int c0 = 32 * ph + 4 * fb + 2 * g;  // chunk of features 256 ph + 32 fb + 16 g
+      *reinterpret_cast<u32x4*>(srow_p + ((c0 ^ (row & 63)) << 4)) = v0;
+      *reinterpret_cast<u32x4*>(srow_p + (((c0 + 1) ^ (row & 63)) << 4)) = v1;
+    }
+  }
+  __syncthreads();
   uint16_t* out_base = p.num_splits == 1
                            ? static_cast<uint16_t*>(p.out_lat)
                            : static_cast<uint16_t*>(p.ws_o) + static_cast<int64_t>(s) * BH * D_C;
-  uint16_t* dst = out_base + bh * D_C + 256 * ph;
 #pragma unroll
-  for (int fb = 0; fb < NFB; fb++) {
-    u32x4 v0, v1;
-#pragma unroll
-    for (int w2 = 0; w2 < 4; w2++) {
-      v0[w2] = pack_bf16x2(O[fb][2 * w2] * inv, O[fb][2 * w2 + 1] * inv);
-      v1[w2] = pack_bf16x2(O[fb][8 + 2 * w2] * inv, O[fb][8 + 2 * w2 + 1] * inv);
+  for (int i = 0; i < A4_HEADS / A4_WAVES; i++) {
+    const int r = (A4_HEADS / A4_WAVES) * wave + i;  // stage row of this instruction
+    const int hr = hg * A4_HEADS + r;
+    if (hr < p.n_h) {
+      const u32x4 v = ld_lds16(tiles + r * (D_C * 2) + ((lane ^ (r & 63)) << 4));
+      st16(out_base + (static_cast<int64_t>(b) * p.n_h + hr) * D_C + 8 * lane, v);
     }
-    uint16_t* o = dst + 32 * fb + 16 * g;
-    st16(o, v0);
-    st16(o + 8, v1);
   }
 }
 
