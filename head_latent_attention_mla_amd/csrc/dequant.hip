@@ -10,7 +10,9 @@
 // 16-byte store), so the 64 lanes of a wave read 512 contiguous bytes and
 // write 1 KiB contiguous bytes per instruction; 8 | 128, so a group lies in
 // a single scale block. Each thread keeps DQ_UNROLL groups in flight (all
-// loads issued before the first conversion); the stores are non-temporal. gfx950's v_cvt_pk_f32_fp8
+// loads issued before the first conversion); the codes are read and the
+// output written non-temporally (each byte is touched once; 9.8 -> 9.45 us
+// for the non-temporal loads on one box). gfx950's v_cvt_pk_f32_fp8
 // decodes OCP E4M3 exactly; the multiply is one fp32 RNE operation and
 // v_cvt_pk_bf16_f32 rounds to nearest-even.
 #include "common.hpp"
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_fp8_block_kernel(
 #pragma unroll
     for (int u = 0; u < DQ_UNROLL; u++) {
       const int64_t gi = min(base + u * DQ_THREADS, n8 - 1);  // past the end: re-read the last
-      c[u] = *reinterpret_cast<const u32x2*>(w + gi * 8);
+      c[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(w + gi * 8));
     }
 #pragma unroll
     for (int u = 0; u < DQ_UNROLL; u++) {
