@@ -51,7 +51,10 @@ def cuda(t):
 # FP8 block dequantisation: bit-exact
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rows,cols", [(512, 4096), (300, 272), (1, 16), (129, 144)])
+# (70001, 512): more 8-code groups than one pass of the launch covers (the
+# grid-stride loop's second pass) and a ragged last 128-row scale block;
+# (300, 272) and (129, 144) end inside a thread's unrolled groups
+@pytest.mark.parametrize("rows,cols", [(512, 4096), (300, 272), (1, 16), (129, 144), (70001, 512)])
 def test_dequant_bit_exact(rows, cols):
     codes = synth.fp8_codes(rows, cols, seed=rows * 7 + cols)
     g = np.random.default_rng(rows + cols)
