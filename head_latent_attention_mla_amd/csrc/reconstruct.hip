@@ -11,22 +11,22 @@
 // N = 8192, n_h = 128: its floor is the MFMA work and the output writes
 // together, so the kernel keeps both busy at once.
 //
-// bf16 path: a persistent kernel, one workgroup of 4 waves per CU, looping
-// over tiles of one head (256 features: the 128 k_nope rows then the 128 v
-// rows) x 256 tokens. Wave (wm, wn) accumulates features 128wm.. x tokens
-// 128wn.. (4 x 4 v_mfma_f32_32x32x16_bf16 tiles, 256 accumulator registers;
-// M = features, N = tokens, K = latent). The latent axis is staged in
-// 32-wide slices (32 KB: 256 weight rows + 256 token rows, 64 bytes each)
-// into four LDS buffers by LDS-DMA issued from inline assembly, three slices
-// ahead of the multiplies and across tile boundaries, so ~96 KB per CU stay
-// in flight. The tile's rotary rows ride along with slices 4..11 into a
-// fifth 32 KB buffer. A tile's epilogue issues its stores (K, V and the
-// rotary copy) and moves straight on: they drain while the next tile
-// multiplies. Every wave issues the same number of memory instructions in
-// the same order (tail tokens re-read and re-write the last token's row with
-// identical values), which makes the vmcnt bookkeeping exact.
-// The A-row permutation pi gives each lane 16 consecutive output features
-// of one token, i.e. two 16-byte stores.
+// bf16 path: one workgroup of 8 waves (two per SIMD) per (head, token chunk);
+// wave w owns output features 32w..32w+31 of the head (waves 0-3 the k_nope
+// rows, 4-7 the v rows) and holds those 32 rows of wkv_b, the MFMA A
+// operands of all 32 k-steps, in registers for the whole kernel (128
+// registers a lane): every weight byte is fetched once per workgroup. The
+// chunk's tokens stream through LDS in stages of 32 whole latent rows (1 KB
+// each, full cache lines; the rotary rows ride along), RW_LEAD stages ahead
+// of the multiplies; per stage a wave runs one chain of 32
+// v_mfma_f32_32x32x16_bf16 (B = the stage's token rows). The A-row order pi
+// gives each lane 16 consecutive features of one token, which go to an LDS
+// output stage (double-buffered) so that every store instruction writes
+// whole rows. Roles split the memory work: waves 0-3 issue all the LDS-DMA
+// (and copy the rotary rows into the output stage), waves 4-7 issue all the
+// stores, five per stage, between their multiplies of the next stage. A
+// loader wave's vector-memory counter then holds only its own DMA, so each
+// stage waits exactly for its group; the storers never wait for a store.
 #include <type_traits>
 
 #include "common.hpp"
@@ -35,246 +35,191 @@
 namespace mla {
 
 namespace {
-constexpr int RC_TOK = 256;                 // tokens per tile
-constexpr int RC_FEAT = ROWS_PER_HEAD;      // 256 features per tile (one head)
-constexpr int RC_KC = 32;                   // latent features per stage
-constexpr int RC_NSTAGE = D_C / RC_KC;      // 16 stages per tile
-constexpr int RC_NBUF = 4;                  // stage buffers
-constexpr int RC_AHEAD = RC_NBUF - 1;       // stages in flight ahead of the multiplies
-constexpr int RC_STAGE_BYTES = (RC_FEAT + RC_TOK) * RC_KC * 2;  // 32 KiB
-constexpr int RC_ROPE_BYTES = RC_TOK * D_R * 2;                 // 32 KiB
-constexpr int RC_LOADS = RC_STAGE_BYTES / 1024 / 4;             // 8 DMA per wave per stage
-constexpr int RC_ROPE_FIRST = 4;            // stages 4..11 also carry one rotary DMA
-constexpr int RC_STORES = 4 * 4 * 2 + RC_TOK * D_R * 2 / 16 / 256;  // 40 per wave per tile
+constexpr int RW_WAVES = 8;                           // waves per workgroup
+constexpr int RW_TOK = 32;                            // tokens per stage
+constexpr int RW_NBUF = 3;                            // staged token buffers
+constexpr int RW_LEAD = RW_NBUF - 1;                  // stages in flight ahead
+constexpr int RW_PITCH = 68 * 16;                     // bytes per staged latent row
+constexpr int RW_LAT_BYTES = RW_TOK * RW_PITCH;       // 34,816
+constexpr int RW_ROPE_BYTES = RW_TOK * D_R * 2;       // 4,096
+constexpr int RW_BUF_BYTES = RW_LAT_BYTES + RW_ROPE_BYTES;
+constexpr int RW_OPITCH = 17 * 16;                    // bytes per staged 128-feature output row
+constexpr int RW_OUT_BYTES = 2 * RW_TOK * RW_OPITCH + RW_ROPE_BYTES;  // k_nope, v, rotary
+constexpr int RW_DMA = RW_TOK / 4 + 1;                // DMA per loader wave and stage
+constexpr int RW_STORES = (2 * RW_TOK * 16 + RW_TOK * 8) / 64 / 4;  // 5 per storer and stage
+constexpr int RW_RING = 4;                            // token operands read ahead
+static_assert(RW_NBUF * RW_BUF_BYTES + 2 * RW_OUT_BYTES <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int pi_row(int i) {
+// Latent row t of a stage starts at chunk rw_shift(t) of its 68-chunk slot: a
+// 16-byte B-operand read of 16 consecutive rows at one chunk then lands in
+// 16 distinct bank quarters ((4t + shift + c) mod 16 is a permutation).
+__device__ __forceinline__ int rw_shift(int t) { return (t >> 2) & 3; }
+// A-operand row i holds feature pi(i) of the wave's 32: accumulator r of lane
+// half g is then feature 16g + r.
+__device__ __forceinline__ int rw_pi(int i) {
   return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
-}
-// DMA instructions per wave of the group that stages slice s of a tile
-constexpr int rc_loads(int s) {
-  return RC_LOADS + (s >= RC_ROPE_FIRST && s < RC_ROPE_FIRST + 8 ? 1 : 0);
-}
-// s_waitcnt vmcnt(N) at the top of stage s: the group of stage s must have
-// landed; the newer memory instructions allowed in flight are the groups of
-// stages s+1 and s+2 and, in the first three stages of a tile, the previous
-// tile's epilogue stores (issued after group s+2 of tile i-1 = group 2 of
-// tile i, before group 3). `prev` is false on a workgroup's first tile (no
-// previous stores), `last` true on its last tile (no groups past stage 15).
-constexpr int rc_wait(int s, bool prev, bool last) {
-  auto L = [&](int t) { return (last && t >= RC_NSTAGE) ? 0 : rc_loads(t % RC_NSTAGE); };
-  const int S = prev ? RC_STORES : 0;
-  if (s == 0) return L(1) + L(2) + S;
-  if (s == 1) return L(2) + S + L(3);
-  if (s == 2) return S + L(3) + L(4);
-  return L(s + 1) + L(s + 2);
 }
 }  // namespace
 
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Output stores: whole 256-byte rows of one token and head (128-byte rows
-// for the rotary copy), non-temporal: the 671 MB of outputs at N = 8192 then
-// do not displace the weight and latent rows later tiles re-read from L2
-// (measured 323 against 362 us with ordinary stores; with the 16-byte
-// pieces of the MFMA layout, non-temporal stores were slower, since L2 then
-// cannot merge the pieces of a line).
-__device__ __forceinline__ void rc_store(uint16_t* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate out of range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// Stage slice k0..k0+31 of the head's 256 weight rows (w_d) and the tile's
-// 256 token rows (x_d; rows past last_row re-read it) into `stage`: chunk j
-// (16 bytes) of row r lands at LDS chunk 4r + (j ^ swz4(r)), weight rows
-// first. Eight DMA instructions per wave.
-__device__ __forceinline__ void rc_stage(i32x4 w_d, i32x4 x_d, int last_row, int k0,
-                                         uint32_t stage, int wave, int lane) {
+// One stage of the loader wave w (0..3): latent rows 8w..8w+7 of the stage
+// (one DMA each, the global row a scalar) and rotary rows 8w..8w+7 (one
+// DMA); tokens past the last re-read it.
+__device__ __forceinline__ void rw_stage(i32x4 c_d, i32x4 r_d, int64_t tok0, int64_t last,
+                                         uint32_t buf, int w, int lane) {
 #pragma unroll
-  for (int k = 0; k < 8; k++) {
-    const int blk = k * 4 + wave;  // 1 KB block of the stage
-    const int pch = (blk & 15) * 64 + lane;
-    const int row = pch >> 2;
-    const int c = (pch & 3) ^ swz4(row);
-    if (k < 4) {
-      dma16(w_d, stage + blk * 1024, static_cast<uint32_t>(row * (D_C * 2) + k0 * 2 + c * 16), 0);
-    } else {
-      const int r = row < last_row ? row : last_row;
-      dma16(x_d, stage + blk * 1024, static_cast<uint32_t>(r * (D_C * 2) + k0 * 2 + c * 16), 0);
-    }
+  for (int k = 0; k < RW_TOK / 4; k++) {
+    const int t = 8 * w + k;
+    const int64_t tk = tok0 + t < last ? tok0 + t : last;
+    dma16(c_d, buf + t * RW_PITCH + 16 * rw_shift(t), static_cast<uint32_t>(lane * 16),
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(tk * (D_C * 2))));
   }
+  const int t = 8 * w + (lane >> 3);
+  const int64_t tk = tok0 + t < last ? tok0 + t : last;
+  dma16(r_d, buf + RW_LAT_BYTES + w * 1024,
+        static_cast<uint32_t>(tk * (D_R * 2)) + static_cast<uint32_t>((lane & 7) * 16), 0);
 }
 
-// Rotary rows of the tile (contiguous 256 x 128 bytes; rows past last_row
-// re-read it): 1 KB block q = 4j + wave, one DMA instruction.
-__device__ __forceinline__ void rc_rope(i32x4 r_d, int last_row, int j, uint32_t rope,
-                                        int wave, int lane) {
-  const int q = 4 * j + wave;
-  const int tok = q * 8 + (lane >> 3);
-  const int t = tok < last_row ? tok : last_row;
-  dma16(r_d, rope + q * 1024, static_cast<uint32_t>(t * (D_R * 2) + (lane & 7) * 16), 0);
-}
-
-__global__ __launch_bounds__(256, 1) void kv_reconstruct_bf16_kernel(
+__global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ k_rope,
     const uint16_t* __restrict__ w, uint16_t* __restrict__ Kout, uint16_t* __restrict__ Vout,
-    int64_t N, int n_h) {
-  __shared__ __attribute__((aligned(16))) char lds[RC_NBUF * RC_STAGE_BYTES + RC_ROPE_BYTES];
-  const int ntt = static_cast<int>((N + RC_TOK - 1) / RC_TOK);
-  const int ntiles = ntt * n_h;
+    int64_t N, int n_h, int chunks, int64_t chunk_tok) {
+  __shared__ __attribute__((aligned(16))) char lds[RW_NBUF * RW_BUF_BYTES + 2 * RW_OUT_BYTES];
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order; renumber
+  // them so that the chunks of one head share an XCD (its weights are then
+  // fetched into one L2).
+  int h, ck;
+  {
+    const int G = static_cast<int>(gridDim.x), L = static_cast<int>(blockIdx.x);
+    const int j = (G & 7) == 0 ? (L & 7) * (G >> 3) + (L >> 3) : L;
+    h = j / chunks;
+    ck = j - h * chunks;
+  }
+  const int64_t tok_begin = static_cast<int64_t>(ck) * chunk_tok;
+  const int64_t tok_end = tok_begin + chunk_tok < N ? tok_begin + chunk_tok : N;
+  if (tok_begin >= tok_end) return;  // (uniform over the workgroup)
+  const int nst = static_cast<int>((tok_end - tok_begin + RW_TOK - 1) / RW_TOK);
+  const int64_t last = N - 1;
+
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;  // feature half (k_nope / v), token half
+  const bool loader = wave < 4;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-  const uint32_t rope_lds = lds0 + RC_NBUF * RC_STAGE_BYTES;
-  const char* rope_buf = lds + RC_NBUF * RC_STAGE_BYTES;
-  // this workgroup's tiles: t = blockIdx.x + i * gridDim.x, i < my_tiles;
-  // tile t = (head t / ntt, token tile t % ntt)
-  const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
-                       static_cast<int>(gridDim.x);
-  if (my_tiles <= 0) return;
+  const i32x4 c_d = make_rsrc(x);
+  const i32x4 r_d = make_rsrc(k_rope);
+  auto buf_addr = [&](int s) { return lds0 + (s % RW_NBUF) * RW_BUF_BYTES; };
+  char* const outs = lds + RW_NBUF * RW_BUF_BYTES;
 
-  struct Tile {
-    i32x4 w_d, x_d, r_d;
-    int last_row, h;
-    int64_t tok0;
-  };
-  auto tile_of = [&](int i) {
-    Tile T;
-    const int t = static_cast<int>(blockIdx.x) + i * static_cast<int>(gridDim.x);
-    T.h = t / ntt;
-    T.tok0 = static_cast<int64_t>(t % ntt) * RC_TOK;
-    T.w_d = make_rsrc(w + static_cast<int64_t>(T.h) * ROWS_PER_HEAD * D_C);
-    T.x_d = make_rsrc(x + T.tok0 * D_C);
-    T.r_d = make_rsrc(k_rope + T.tok0 * D_R);
-    T.last_row = static_cast<int>(N - 1 - T.tok0 < RC_TOK - 1 ? N - 1 - T.tok0 : RC_TOK - 1);
-    return T;
-  };
-  // the DMA group of stage s of tile T into buffer slot
-  auto issue = [&](const Tile& T, int s, int slot) {
-    rc_stage(T.w_d, T.x_d, T.last_row, s * RC_KC, lds0 + slot * RC_STAGE_BYTES, wave, lane);
-    if (s >= RC_ROPE_FIRST && s < RC_ROPE_FIRST + 8)
-      rc_rope(T.r_d, T.last_row, s - RC_ROPE_FIRST, rope_lds, wave, lane);
-  };
+  // the first RW_LEAD stages in flight, then this wave's 32 weight rows
+  if (loader) {
+#pragma unroll
+    for (int s = 0; s < RW_LEAD; s++)
+      if (s < nst) rw_stage(c_d, r_d, tok_begin + s * RW_TOK, last, buf_addr(s), wave, lane);
+  }
+  bf16x8 A[D_C / 16];
+  {
+    const uint16_t* wr =
+        w + (static_cast<int64_t>(h) * ROWS_PER_HEAD + 32 * wave + rw_pi(n)) * D_C + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < D_C / 16; ks++) A[ks] = as_bf16x8(ld16(wr + 16 * ks));
+  }
+  // consume the weight loads here (the wait also covers the older DMA)
+#pragma unroll
+  for (int ks = 0; ks < D_C / 16; ks++) asm volatile("" : : "v"(A[ks]));
 
-  floatx16 acc[4][4];
-  Tile cur = tile_of(0);
-  // prologue: groups of stages 0..2 of the first tile (slots 0..2)
-#pragma unroll
-  for (int s = 0; s < RC_AHEAD; s++) issue(cur, s, s);
+  // B operands: token row n, chunk 2ks + g
+  const int b_off = n * RW_PITCH + 16 * (rw_shift(n) + g);
+  // output stage row of this lane: token n, chunks 4(wave % 4) + 2g, +1
+  const int o_off = (loader ? 0 : RW_TOK * RW_OPITCH) + n * RW_OPITCH;
+  const int o_c0 = 4 * (wave & 3) + 2 * g;
 
-  int gstage = 0;  // stages begun so far (the buffer slot is gstage % RC_NBUF)
-  for (int i = 0; i < my_tiles; i++) {
-    const bool prev = i > 0, last = i + 1 == my_tiles;
-    Tile nxt = last ? cur : tile_of(i + 1);
+  // the storers' five stores of one stage: instruction j = 4i + (wave - 4)
+  // of 20 (8 k_nope, 8 v, 4 rotary)
+  u32x4 sv[RW_STORES];
+  uint16_t* sp[RW_STORES];
+  bool sok[RW_STORES];
+  auto load_stores = [&](int s) {
+    const char* ob = outs + (s & 1) * RW_OUT_BYTES;
+    const int64_t tok0 = tok_begin + static_cast<int64_t>(s) * RW_TOK;
 #pragma unroll
-    for (int a = 0; a < 4; a++)
-#pragma unroll
-      for (int b = 0; b < 4; b++) acc[a][b] = floatx16{};
-    static_for<0, RC_NSTAGE>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      // group s landed; stage s-1's buffer is free for the group 3 ahead
-      if (prev && !last) wait_vm<rc_wait(s, true, false)>();
-      else if (prev) wait_vm<rc_wait(s, true, true)>();
-      else if (!last) wait_vm<rc_wait(s, false, false)>();
-      else wait_vm<rc_wait(s, false, true)>();
-      __syncthreads();
-      const int ahead = s + RC_AHEAD;
-      const int slot_ahead = (gstage + RC_AHEAD) & (RC_NBUF - 1);
-      if (ahead < RC_NSTAGE)
-        issue(cur, ahead, slot_ahead);
-      else if (!last)
-        issue(nxt, ahead - RC_NSTAGE, slot_ahead);
-      const char* buf = lds + (gstage & (RC_NBUF - 1)) * RC_STAGE_BYTES;
-      gstage++;
-#pragma unroll
-      for (int ks = 0; ks < RC_KC / 16; ks++) {
-        const int c = 2 * ks + g;
-        bf16x8 av[4], bv[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-          const int row = wm * 128 + mt * 32 + pi_row(n);
-          av[mt] = as_bf16x8(ld_lds16(buf + (row * 4 + (c ^ swz4(row))) * 16));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; nt++) {
-          const int row = wn * 128 + nt * 32 + n;
-          bv[nt] = as_bf16x8(ld_lds16(buf + RC_FEAT * RC_KC * 2 + (row * 4 + (c ^ swz4(row))) * 16));
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-          for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma32x32x16(av[mt], bv[nt], acc[mt][nt]);
+    for (int i = 0; i < RW_STORES; i++) {
+      const int j = 4 * i + (wave - 4);
+      int t, c;
+      const char* src;
+      if (j < 16) {  // k_nope (j < 8) or v rows: 4 tokens x 16 chunks
+        t = 4 * (j & 7) + (lane >> 4);
+        c = lane & 15;
+        src = ob + (j < 8 ? 0 : RW_TOK * RW_OPITCH) + t * RW_OPITCH + 16 * c;
+      } else {  // rotary rows: 8 tokens x 8 chunks
+        t = 8 * (j - 16) + (lane >> 3);
+        c = lane & 7;
+        src = ob + 2 * RW_TOK * RW_OPITCH + t * 128 + 16 * c;
       }
-    });
-    // K[n,h,128:192] = k_rope[n,:] from the staged rows: 8 chunks per token
-#pragma unroll
-    for (int k = 0; k < RC_TOK * 8 / 256; k++) {
-      const int idx = k * 256 + static_cast<int>(threadIdx.x);
-      const int tl = min(idx >> 3, cur.last_row);
-      const u32x4 v = ld_lds16(rope_buf + (idx >> 3) * 128 + (idx & 7) * 16);
-      rc_store(Kout + ((cur.tok0 + tl) * n_h + cur.h) * (D_N + D_R) + D_N + (idx & 7) * 8, v);
+      const int64_t tk = tok0 + t;
+      sok[i] = tk < tok_end;
+      const int64_t row = (sok[i] ? tk : tok_begin) * n_h + h;
+      sp[i] = j < 8 ? Kout + row * (D_N + D_R) + 8 * c
+            : j < 16 ? Vout + row * D_V + 8 * c
+                     : Kout + row * (D_N + D_R) + D_N + 8 * c;
+      sv[i] = ld_lds16(src);
     }
-    // every wave is done with the rotary rows: the buffer now stages each
-    // wave's outputs (8 KB per wave), so that every store instruction writes
-    // whole 256-byte rows (4 tokens) instead of 64 separate 16-byte pieces.
-    // The buffer is next written by the rotary DMA issued after the barrier
-    // of the next tile's stage 1.
+  };
+  auto store = [&](int i) {
+    if (sok[i]) __builtin_nontemporal_store(sv[i], reinterpret_cast<u32x4*>(sp[i]));
+  };
+
+  for (int s = 0; s < nst; s++) {
+    // stage s landed (a loader's counter holds only its DMA: the groups of
+    // stages s .. s+RW_LEAD-1 that exist)
+    if (loader) {
+      if (s + 1 < nst)
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(RW_DMA) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // stage s published; every wave is done with stage s-1's buffer, and the
+    // output stage of s-1 is complete
     __syncthreads();
-    char* stg = const_cast<char*>(rope_buf) + wave * 8192;
+    if (loader && s + RW_LEAD < nst)
+      rw_stage(c_d, r_d, tok_begin + static_cast<int64_t>(s + RW_LEAD) * RW_TOK, last,
+               buf_addr(s + RW_LEAD), wave, lane);
+    const bool st = !loader && s > 0;
+    if (st) load_stores(s - 1);
+    const char* bp = lds + (s % RW_NBUF) * RW_BUF_BYTES + b_off;
+    floatx16 acc = {};
+    u32x4 ring[RW_RING];
 #pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-      // lane (token n of N-tile nt, half g) holds features 32mt + 16g .. +15
-      // of half wm: chunks 4mt + 2g, +1 of the token's 16-chunk row,
-      // XOR-swizzled by token
+    for (int j = 0; j < RW_RING; j++) ring[j] = ld_lds16(bp + 32 * j);
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        u32x4 v0, v1;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; w2++) {
-          v0[w2] = pack_bf16x2(acc[mt][nt][2 * w2], acc[mt][nt][2 * w2 + 1]);
-          v1[w2] = pack_bf16x2(acc[mt][nt][8 + 2 * w2], acc[mt][nt][8 + 2 * w2 + 1]);
-        }
-        const int c0 = 4 * mt + 2 * g;
-        *reinterpret_cast<u32x4*>(stg + n * 256 + ((c0 ^ (n & 15)) << 4)) = v0;
-        *reinterpret_cast<u32x4*>(stg + n * 256 + (((c0 + 1) ^ (n & 15)) << 4)) = v1;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // 16 lanes per token row: tokens 4i + lane/16, chunk lane % 16; tail
-      // tokens rewrite the last token's row with identical values
-      u32x4 rows[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int r = 4 * i + (lane >> 4), c = lane & 15;
-        rows[i] = ld_lds16(stg + r * 256 + ((c ^ (r & 15)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int r = 4 * i + (lane >> 4), c = lane & 15;
-        const int64_t tk = cur.tok0 + min(wn * 128 + nt * 32 + r, cur.last_row);
-        uint16_t* dst = wm == 0 ? Kout + (tk * n_h + cur.h) * (D_N + D_R) + c * 8
-                                : Vout + (tk * n_h + cur.h) * D_V + c * 8;
-        rc_store(dst, rows[i]);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int ks = 0; ks < D_C / 16; ks++) {
+      const u32x4 b = ring[ks % RW_RING];
+      if (ks + RW_RING < D_C / 16) ring[ks % RW_RING] = ld_lds16(bp + 32 * (ks + RW_RING));
+      if (st && ks < RW_STORES) store(ks);
+      acc = mfma32x32x16(A[ks], as_bf16x8(b), acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    cur = nxt;
+    // this wave's 32 features of the 32 tokens into output stage s & 1
+    char* ob = outs + (s & 1) * RW_OUT_BYTES;
+    {
+      u32x4 v0, v1;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        v0[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
+        v1[k] = pack_bf16x2(acc[8 + 2 * k], acc[8 + 2 * k + 1]);
+      }
+      *reinterpret_cast<u32x4*>(ob + o_off + 16 * o_c0) = v0;
+      *reinterpret_cast<u32x4*>(ob + o_off + 16 * (o_c0 + 1)) = v1;
+    }
+    if (loader) {  // rotary rows 8w..8w+7 of the stage into the output stage
+      const char* rb = lds + (s % RW_NBUF) * RW_BUF_BYTES + RW_LAT_BYTES + wave * 1024;
+      *reinterpret_cast<u32x4*>(ob + 2 * RW_TOK * RW_OPITCH + wave * 1024 + 16 * lane) =
+          ld_lds16(rb + 16 * lane);
+    }
+  }
+  __syncthreads();
+  if (!loader) {
+    load_stores(nst - 1);
+#pragma unroll
+    for (int i = 0; i < RW_STORES; i++) store(i);
   }
 }
 
@@ -318,12 +263,20 @@ static int cu_count() {
 hipError_t launch_kv_reconstruct(const void* c, const void* k_rope, const void* wkv_b, void* K,
                                  void* V, int64_t N, int n_h, bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
-    const int64_t tiles = (N + RC_TOK - 1) / RC_TOK * n_h;
-    const int64_t grid = tiles < cu_count() ? tiles : cu_count();
-    hipLaunchKernelGGL(kv_reconstruct_bf16_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       stream, static_cast<const uint16_t*>(c),
+    // token chunks per head: enough (head, chunk) workgroups to fill the CUs,
+    // each chunk a whole number of 32-token stages
+    const int cus = cu_count();
+    int64_t chunks = n_h < cus ? cus / n_h : 1;
+    const int64_t stages = (N + RW_TOK - 1) / RW_TOK;
+    if (chunks > stages) chunks = stages;
+    const int64_t chunk_tok = (stages + chunks - 1) / chunks * RW_TOK;
+    chunks = (N + chunk_tok - 1) / chunk_tok;
+    const int64_t grid = static_cast<int64_t>(n_h) * chunks;
+    hipLaunchKernelGGL(kv_reconstruct_bf16_kernel, dim3(static_cast<unsigned>(grid)),
+                       dim3(RW_WAVES * 64), 0, stream, static_cast<const uint16_t*>(c),
                        static_cast<const uint16_t*>(k_rope), static_cast<const uint16_t*>(wkv_b),
-                       static_cast<uint16_t*>(K), static_cast<uint16_t*>(V), N, n_h);
+                       static_cast<uint16_t*>(K), static_cast<uint16_t*>(V), N, n_h,
+                       static_cast<int>(chunks), chunk_tok);
   } else {
     hipLaunchKernelGGL(kv_reconstruct_f32_kernel, dim3(static_cast<unsigned>(N * n_h)), dim3(256), 0,
                        stream, static_cast<const float*>(c), static_cast<const float*>(k_rope),
