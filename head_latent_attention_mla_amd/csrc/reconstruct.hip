@@ -133,41 +133,77 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
   const int o_c0 = 4 * (wave & 3) + 2 * g;
 
   // the storers' five stores of one stage: instruction j = 4i + (wave - 4)
-  // of 20 (8 k_nope, 8 v, 4 rotary)
-  u32x4 sv[RW_STORES];
+  // of 20 (8 k_nope, 8 v, 4 rotary). Per instruction the lane's token t of
+  // the stage, its source in the output stage and its destination for the
+  // chunk's first stage (later stages: + 32 tokens of rows each)
+  int st_t[RW_STORES], st_src[RW_STORES];
   uint16_t* sp[RW_STORES];
+  int64_t st_step[RW_STORES];
+#pragma unroll
+  for (int i = 0; i < RW_STORES; i++) {
+    const int j = 4 * i + ((wave - 4) & 3);
+    int c;
+    if (j < 16) {  // k_nope (j < 8) or v rows: 4 tokens x 16 chunks
+      st_t[i] = 4 * (j & 7) + (lane >> 4);
+      c = lane & 15;
+      st_src[i] = (j < 8 ? 0 : RW_TOK * RW_OPITCH) + st_t[i] * RW_OPITCH + 16 * c;
+    } else {  // rotary rows: 8 tokens x 8 chunks
+      st_t[i] = 8 * (j - 16) + (lane >> 3);
+      c = lane & 7;
+      st_src[i] = 2 * RW_TOK * RW_OPITCH + st_t[i] * 128 + 16 * c;
+    }
+    const int64_t row = (tok_begin + st_t[i]) * n_h + h;
+    sp[i] = j < 8 ? Kout + row * (D_N + D_R) + 8 * c
+          : j < 16 ? Vout + row * D_V + 8 * c
+                   : Kout + row * (D_N + D_R) + D_N + 8 * c;
+    st_step[i] = static_cast<int64_t>(RW_TOK) * n_h * (j >= 8 && j < 16 ? D_V : D_N + D_R);
+  }
+  u32x4 sv[RW_STORES];
   bool sok[RW_STORES];
+  // outputs of stage s (s = 0, 1, ... in order): read from the output stage
   auto load_stores = [&](int s) {
     const char* ob = outs + (s & 1) * RW_OUT_BYTES;
-    const int64_t tok0 = tok_begin + static_cast<int64_t>(s) * RW_TOK;
+    const int64_t left = tok_end - (tok_begin + static_cast<int64_t>(s) * RW_TOK);
 #pragma unroll
     for (int i = 0; i < RW_STORES; i++) {
-      const int j = 4 * i + (wave - 4);
-      int t, c;
-      const char* src;
-      if (j < 16) {  // k_nope (j < 8) or v rows: 4 tokens x 16 chunks
-        t = 4 * (j & 7) + (lane >> 4);
-        c = lane & 15;
-        src = ob + (j < 8 ? 0 : RW_TOK * RW_OPITCH) + t * RW_OPITCH + 16 * c;
-      } else {  // rotary rows: 8 tokens x 8 chunks
-        t = 8 * (j - 16) + (lane >> 3);
-        c = lane & 7;
-        src = ob + 2 * RW_TOK * RW_OPITCH + t * 128 + 16 * c;
-      }
-      const int64_t tk = tok0 + t;
-      sok[i] = tk < tok_end;
-      const int64_t row = (sok[i] ? tk : tok_begin) * n_h + h;
-      sp[i] = j < 8 ? Kout + row * (D_N + D_R) + 8 * c
-            : j < 16 ? Vout + row * D_V + 8 * c
-                     : Kout + row * (D_N + D_R) + D_N + 8 * c;
-      sv[i] = ld_lds16(src);
+      sok[i] = st_t[i] < left;
+      sv[i] = ld_lds16(ob + st_src[i]);
     }
   };
+  // store i, then on to the same rows of the next stage
   auto store = [&](int i) {
     if (sok[i]) __builtin_nontemporal_store(sv[i], reinterpret_cast<u32x4*>(sp[i]));
+    sp[i] += st_step[i];
   };
 
-  for (int s = 0; s < nst; s++) {
+  // this wave's 32 features of the 32 tokens of stage s into output stage s & 1
+  auto write_out = [&](int s, const floatx16& acc) {
+    char* ob = outs + (s & 1) * RW_OUT_BYTES;
+    u32x4 v0, v1;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v0[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
+      v1[k] = pack_bf16x2(acc[8 + 2 * k], acc[8 + 2 * k + 1]);
+    }
+    *reinterpret_cast<u32x4*>(ob + o_off + 16 * o_c0) = v0;
+    *reinterpret_cast<u32x4*>(ob + o_off + 16 * (o_c0 + 1)) = v1;
+  };
+  // loaders: rotary rows 8w..8w+7 of stage s, from its token buffer into
+  // output stage s & 1
+  auto read_rope = [&](int s) {
+    return ld_lds16(lds + (s % RW_NBUF) * RW_BUF_BYTES + RW_LAT_BYTES + wave * 1024 + 16 * lane);
+  };
+  auto write_rope = [&](int s, u32x4 v) {
+    *reinterpret_cast<u32x4*>(outs + (s & 1) * RW_OUT_BYTES + 2 * RW_TOK * RW_OPITCH +
+                              wave * 1024 + 16 * lane) = v;
+  };
+
+  // Stage s. The outputs of stage s-1 (accumulators `prev`) go to the output
+  // stage between the first multiplies of stage s, and the storers store
+  // those of stage s-2 (complete since the barrier) between the multiplies;
+  // the loaders move stage s-1's rotary rows out of its token buffer before
+  // they refill that buffer with stage s+RW_LEAD.
+  auto body = [&](int s, floatx16& acc, const floatx16& prev) {
     // stage s landed (a loader's counter holds only its DMA: the groups of
     // stages s .. s+RW_LEAD-1 that exist)
     if (loader) {
@@ -176,16 +212,14 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // stage s published; every wave is done with stage s-1's buffer, and the
-    // output stage of s-1 is complete
+    // stage s published; every wave is done with stage s-1's token buffer and
+    // the output stage of s-2 is complete
     __syncthreads();
-    if (loader && s + RW_LEAD < nst)
-      rw_stage(c_d, r_d, tok_begin + static_cast<int64_t>(s + RW_LEAD) * RW_TOK, last,
-               buf_addr(s + RW_LEAD), wave, lane);
-    const bool st = !loader && s > 0;
-    if (st) load_stores(s - 1);
+    const bool st = !loader && s >= 2;
+    if (st) load_stores(s - 2);
+    u32x4 rope = {};
+    if (loader && s >= 1) rope = read_rope(s - 1);
     const char* bp = lds + (s % RW_NBUF) * RW_BUF_BYTES + b_off;
-    floatx16 acc = {};
     u32x4 ring[RW_RING];
 #pragma unroll
     for (int j = 0; j < RW_RING; j++) ring[j] = ld_lds16(bp + 32 * j);
@@ -193,27 +227,39 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
     for (int ks = 0; ks < D_C / 16; ks++) {
       const u32x4 b = ring[ks % RW_RING];
       if (ks + RW_RING < D_C / 16) ring[ks % RW_RING] = ld_lds16(bp + 32 * (ks + RW_RING));
-      if (st && ks < RW_STORES) store(ks);
-      acc = mfma32x32x16(A[ks], as_bf16x8(b), acc);
+      if (ks == 1 && s >= 1) {
+        write_out(s - 1, prev);
+        if (loader) write_rope(s - 1, rope);
+      }
+      // (the rotary rows were read and written back at ks = 1: the buffer
+      // is free for the DMA)
+      if (ks == 4 && loader && s + RW_LEAD < nst)
+        rw_stage(c_d, r_d, tok_begin + static_cast<int64_t>(s + RW_LEAD) * RW_TOK, last,
+                 buf_addr(s + RW_LEAD), wave, lane);
+      if (st && ks % 6 == 3 && ks / 6 < RW_STORES) store(ks / 6);
+      acc = mfma32x32x16(A[ks], as_bf16x8(b), ks == 0 ? floatx16{} : acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // this wave's 32 features of the 32 tokens into output stage s & 1
-    char* ob = outs + (s & 1) * RW_OUT_BYTES;
-    {
-      u32x4 v0, v1;
+  };
+  floatx16 acc0 = {}, acc1 = {};
+  for (int s = 0; s < nst; s += 2) {
+    body(s, acc0, acc1);
+    if (s + 1 < nst) body(s + 1, acc1, acc0);
+  }
+  // the last two stages' outputs: nst-2 (written during stage nst-1) and
+  // nst-1 (still in registers)
+  __syncthreads();
+  if (!loader && nst >= 2) {
+    load_stores(nst - 2);
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        v0[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
-        v1[k] = pack_bf16x2(acc[8 + 2 * k], acc[8 + 2 * k + 1]);
-      }
-      *reinterpret_cast<u32x4*>(ob + o_off + 16 * o_c0) = v0;
-      *reinterpret_cast<u32x4*>(ob + o_off + 16 * (o_c0 + 1)) = v1;
-    }
-    if (loader) {  // rotary rows 8w..8w+7 of the stage into the output stage
-      const char* rb = lds + (s % RW_NBUF) * RW_BUF_BYTES + RW_LAT_BYTES + wave * 1024;
-      *reinterpret_cast<u32x4*>(ob + 2 * RW_TOK * RW_OPITCH + wave * 1024 + 16 * lane) =
-          ld_lds16(rb + 16 * lane);
-    }
+    for (int i = 0; i < RW_STORES; i++) store(i);
+  }
+  {
+    const floatx16 lastacc = (nst - 1) & 1 ? acc1 : acc0;
+    u32x4 rope = {};
+    if (loader) rope = read_rope(nst - 1);
+    write_out(nst - 1, lastacc);
+    if (loader) write_rope(nst - 1, rope);
   }
   __syncthreads();
   if (!loader) {
