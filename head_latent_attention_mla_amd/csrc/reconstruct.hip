@@ -62,21 +62,26 @@ __device__ __forceinline__ int rw_pi(int i) {
 }  // namespace
 
 // One stage of the loader wave w (0..3): latent rows 8w..8w+7 of the stage
-// (one DMA each, the global row a scalar) and rotary rows 8w..8w+7 (one
-// DMA); tokens past the last re-read it.
-__device__ __forceinline__ void rw_stage(i32x4 c_d, i32x4 r_d, int64_t tok0, int64_t last,
-                                         uint32_t buf, int w, int lane) {
+// (one DMA each, the row's offset a scalar) and rotary rows 8w..8w+7 (one
+// DMA); tokens past the last re-read it. The buffer descriptors are based at
+// the stage's first token, so every offset stays below 32 KB however long
+// the sequence.
+__device__ __forceinline__ void rw_stage(const uint16_t* x, const uint16_t* k_rope, int64_t tok0,
+                                         int64_t last, uint32_t buf, int w, int lane) {
+  const i32x4 c_d = make_rsrc(x + tok0 * D_C);
+  const i32x4 r_d = make_rsrc(k_rope + tok0 * D_R);
+  const int lastr = static_cast<int>(last - tok0 < RW_TOK - 1 ? last - tok0 : RW_TOK - 1);
 #pragma unroll
   for (int k = 0; k < RW_TOK / 4; k++) {
     const int t = 8 * w + k;
-    const int64_t tk = tok0 + t < last ? tok0 + t : last;
+    const int tr = t < lastr ? t : lastr;
     dma16(c_d, buf + t * RW_PITCH + 16 * rw_shift(t), static_cast<uint32_t>(lane * 16),
-          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(tk * (D_C * 2))));
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(tr * (D_C * 2))));
   }
   const int t = 8 * w + (lane >> 3);
-  const int64_t tk = tok0 + t < last ? tok0 + t : last;
+  const int tr = t < lastr ? t : lastr;
   dma16(r_d, buf + RW_LAT_BYTES + w * 1024,
-        static_cast<uint32_t>(tk * (D_R * 2)) + static_cast<uint32_t>((lane & 7) * 16), 0);
+        static_cast<uint32_t>(tr * (D_R * 2) + (lane & 7) * 16), 0);
 }
 
 __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
@@ -104,8 +109,6 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
   const int n = lane & 31, g = lane >> 5;
   const bool loader = wave < 4;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-  const i32x4 c_d = make_rsrc(x);
-  const i32x4 r_d = make_rsrc(k_rope);
   auto buf_addr = [&](int s) { return lds0 + (s % RW_NBUF) * RW_BUF_BYTES; };
   char* const outs = lds + RW_NBUF * RW_BUF_BYTES;
 
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
   if (loader) {
 #pragma unroll
     for (int s = 0; s < RW_LEAD; s++)
-      if (s < nst) rw_stage(c_d, r_d, tok_begin + s * RW_TOK, last, buf_addr(s), wave, lane);
+      if (s < nst) rw_stage(x, k_rope, tok_begin + s * RW_TOK, last, buf_addr(s), wave, lane);
   }
   bf16x8 A[D_C / 16];
   {
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(RW_WAVES * 64, 1) void kv_reconstruct_bf16_kernel(
       // (the rotary rows were read and written back at ks = 1: the buffer
       // is free for the DMA)
       if (ks == 4 && loader && s + RW_LEAD < nst)
-        rw_stage(c_d, r_d, tok_begin + static_cast<int64_t>(s + RW_LEAD) * RW_TOK, last,
+        rw_stage(x, k_rope, tok_begin + static_cast<int64_t>(s + RW_LEAD) * RW_TOK, last,
                  buf_addr(s + RW_LEAD), wave, lane);
       if (st && ks % 6 == 3 && ks / 6 < RW_STORES) store(ks / 6);
       acc = mfma32x32x16(A[ks], as_bf16x8(b), ks == 0 ? floatx16{} : acc);

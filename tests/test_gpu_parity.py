@@ -309,6 +309,33 @@ def test_kv_reconstruct(N, n_h, dtype):
     assert torch.equal(host(K)[..., 128:], inp["k_rope"][:, None, :].expand(N, n_h, 64))
 
 
+def test_kv_reconstruct_latent_beyond_two_gib():
+    """One head over 2.2M tokens: the latent array is 2.25 GB, so rows past
+    the first 2 GiB must be addressed correctly. The rows repeat a seeded
+    block of 4099 (tiled on the device; 4099 divides no power of two, so a
+    row fetched from a wrapped or clamped offset holds other values); sampled
+    tokens around the 2 GiB mark and at the end are checked against the
+    oracle."""
+    N, P, n_h = 2_200_000, 4099, 1
+    inp = synth.reconstruct_inputs(P, n_h, torch.bfloat16, seed=4099)
+    reps = -(-N // P)
+    c = cuda(inp["c"]).repeat(reps, 1)[:N].contiguous()
+    kr = cuda(inp["k_rope"]).repeat(reps, 1)[:N].contiguous()
+    K, V = mla.mla_kv_reconstruct(c, kr, cuda(inp["wkv_b"]))
+    del c, kr
+    edge = 1 << 21  # token whose latent row starts at byte 2 GiB
+    rows = np.concatenate([[0, edge - 1, edge, edge + 1, N - 1],
+                           np.random.default_rng(7).choice(N, 27, replace=False)])
+    rows = np.unique(rows)
+    src = torch.from_numpy(rows % P)
+    Kr, Vr = oracle.kv_reconstruct(inp["c"][src], inp["k_rope"][src], inp["wkv_b"], n_h)
+    idx = torch.from_numpy(rows).to(K.device)
+    Kg, Vg = host(K[idx]), host(V[idx])
+    check(Kg[..., :128].double().numpy(), Kr[..., :128], BF16_TOL, "k_nope")
+    check(Vg.double().numpy(), Vr, BF16_TOL, "v")
+    assert torch.equal(Kg[..., 128:], inp["k_rope"][src][:, None, :])
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------
