@@ -154,10 +154,10 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
     int64_t bh[2] = {static_cast<int64_t>(b0) * n_h + h, static_cast<int64_t>(b1) * n_h + h};
     int nrows = 0;
     if (b1 < B) {
-      merge_rows8<2>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+      merge_rows8<2, true>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
       nrows = 2;
     } else if (b0 < B) {
-      merge_rows8<1>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
+      merge_rows8<1, true>(ws_o, ws_lse, S, BH, bh, lane * 8, o8, l);
       nrows = 1;
     }
 #pragma unroll
