@@ -232,7 +232,10 @@ def reconstruct_main(args, torch, mla, synth):
     inp = synth.config_inputs(5)
     base = {k: v.to(dev) for k, v in inp.items()}
     per_rep = sum(v.numel() * v.element_size() for v in base.values())
-    R = max(2, int(-(-args.min_replica_bytes // per_rep)))
+    w_bytes = base["wkv_b"].numel() * base["wkv_b"].element_size()
+    # (the weights alone also above the bound: see the decode replicas)
+    R = max(2, int(-(-args.min_replica_bytes // per_rep)),
+            int(-(-args.min_replica_bytes // w_bytes)))
     reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
     K = torch.empty((N, n_h, 192), dtype=torch.bfloat16, device=dev)
     V = torch.empty((N, n_h, 128), dtype=torch.bfloat16, device=dev)
@@ -496,9 +499,12 @@ def main():
                 topk=inp["topk_idx"].to(dev) if sparse else None)
     per_rep = (base["cache"].numel() * 2 + w0.numel() * 2 if not sparse
                else B * rows * 576 * 2 + w0.numel() * 2)
-    R = max(2, int(-(-args.min_replica_bytes // per_rep)))
-    if sparse:
-        R = max(R, 2)
+    # enough replicas that the weights alone also exceed the bound: the cache
+    # rows are read with the non-temporal hint, so a few replicas' weights
+    # could otherwise stay in the 256 MB Infinity Cache from one round to the
+    # next (a model's layers each have their own wkv_b)
+    R = max(2, int(-(-args.min_replica_bytes // per_rep)),
+            int(-(-args.min_replica_bytes // (w0.numel() * 2))))
     reps = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
                      for _ in range(R - 1)]
     q_lat = torch.empty((B, n_h, 512), dtype=torch.bfloat16, device=dev)
