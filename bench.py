@@ -11,9 +11,9 @@ sequence.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
 synchronisation, HIP events on the stream the kernels run on, replayed from
-HIP graphs of ~30 steps. Each step uses the next of R device replicas of the
-inputs (>= 1 GiB in total) so the 256 MB Infinity Cache cannot serve the
-cache reads. The roofline object reports the stand-alone attention call
+HIP graphs of >= 60 steps (one per layer of a 61-layer decode graph). Each
+step uses the next of R device replicas of the inputs (cache and weights each
+>= 1.1 GB in total) so the 256 MB Infinity Cache cannot serve them. The roofline object reports the stand-alone attention call
 (split + merge kernels; with whole 128-head groups on the packed queries the
 step's attention kernel reads), timed per call from graphs of R and 3R
 calls.
@@ -627,10 +627,10 @@ def main():
     # timed region: exactly K whole steps, bracketed by synchronisation,
     # replayed from HIP graphs of G consecutive steps cycling over the R input
     # replicas, plus one graph for the remaining K mod G steps; G is whole
-    # rounds over the replicas, about 30 steps (a multi-layer decode graph
-    # holds as many), so the fixed cost of launching a graph is spread as it
-    # would be there
-    G = R * max(1, 30 // R)
+    # rounds over the replicas, at least 60 steps (a decode graph of a
+    # 61-layer model holds one attention step per layer), so the fixed cost
+    # of launching a graph is spread as it would be there
+    G = R * max(1, -(-60 // R))
     full, rest = divmod(args.steps, G)
     if not args.no_graph:
         g_full = graph_of(step, G)
