@@ -137,9 +137,9 @@ def cpu_baseline(cfg, inp):
                       f"fp64 C oracle, OpenMP over (sequence, head)"}
 
 
-INPUT_NOTE = ("latent rows drawn N(0,1) per feature (row RMS 1 +- 0.03, the spread of a "
-              "normalised latent; not renormalised), rotary keys and queries N(0,1), "
-              "wkv_b N(0,1/512)")
+INPUT_NOTE = ("latent rows of unit RMS (512 standard normals scaled to RMS 1: how an "
+              "RMS-normalised standard normal row with unit gain is distributed), rotary "
+              "keys and queries N(0,1), wkv_b N(0,1/512)")
 
 
 def batch_stats(torch, replay, n_batches, steps_per_batch):

@@ -9,9 +9,12 @@ Recipe (one numpy PCG64 stream per tensor, spawned from one SeedSequence,
 in the fixed order latent, rope, q_nope, q_pe, wkv_b, scales, top-k, then
 the stand-alone stage inputs q_lat and o_lat, then the cache-append inputs
 kv_a, gain, angles, positions):
-  latent   ~ N(0,1) in float32: the spread of the normalised KV latent the
-           cache holds (the root mean square of 512 standard normals is
-           1 +- 0.03; no normalisation is applied here).
+  latent   rows of 512 standard normals, each scaled (float64) to a root
+           mean square of exactly 1: a uniformly random direction on the
+           sphere of radius sqrt(512), which is how an RMS-normalised
+           standard normal row with unit gain is distributed (the eps of the
+           norm moves the RMS by ~1e-6). Drawing it this way is sampling,
+           not the cache-append arithmetic (no gain, no eps).
   rope     ~ N(0,1)           (already-rotated shared key)
   q_nope   ~ N(0,1), q_pe ~ N(0,1)
   wkv_b    ~ N(0, 1/512)  [n_h*256, 512], stored [out, in]
@@ -62,6 +65,13 @@ def _normal(g, shape, std=1.0):
     return x
 
 
+def _unit_rms_rows(g, shape):
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    ms = np.einsum("...i,...i->...", x, x, dtype=np.float64) / shape[-1]
+    x *= (1.0 / np.sqrt(ms)).astype(np.float32)[..., None]
+    return x
+
+
 def _store(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(x))
     return t if dtype == torch.float32 else t.to(dtype)
@@ -83,7 +93,7 @@ def decode_inputs(B: int, n_h: int, T: int, dtype=torch.bfloat16, seed: int = 0,
     """
     g = _streams(seed)
     cache = np.empty((B, T, D_C + D_R), np.float32)
-    cache[..., :D_C] = _normal(g["latent"], (B, T, D_C))
+    cache[..., :D_C] = _unit_rms_rows(g["latent"], (B, T, D_C))
     cache[..., D_C:] = _normal(g["rope"], (B, T, D_R))
     out = {
         "cache": _store(cache, dtype),
@@ -116,7 +126,7 @@ def reconstruct_inputs(N: int, n_h: int, dtype=torch.bfloat16, seed: int = 0) ->
     """c [N, 512], k_rope [N, 64], wkv_b [n_h*256, 512]."""
     g = _streams(seed)
     return {
-        "c": _store(_normal(g["latent"], (N, D_C)), dtype),
+        "c": _store(_unit_rms_rows(g["latent"], (N, D_C)), dtype),
         "k_rope": _store(_normal(g["rope"], (N, D_R)), dtype),
         "wkv_b": _store(_normal(g["wkv_b"], (n_h * (D_N + D_V), D_C), std=512 ** -0.5), dtype),
     }
