@@ -93,6 +93,29 @@ __device__ __forceinline__ void merge_rows8(const uint16_t* __restrict__ ws_o,
     load(0, MERGE_CHUNK, l1, v1);
     merge_fold8(l0, v0, 0, S, mx[0], wsum[0], acc[0]);
     merge_fold8(l1, v1, MERGE_CHUNK, S, mx[0], wsum[0], acc[0]);
+  } else if (NR == 1 && S > 2 * MERGE_CHUNK) {
+    // one row of many splits (long positions over few sequences): MERGE_AHEAD
+    // chunks in flight, chunk c + MERGE_AHEAD loaded right after chunk c is
+    // folded; the chunks are folded in order, so the result is the bits of
+    // one chunk per round trip (measured at B=4 T=32768, 64 splits: the
+    // round trips were the merge's time)
+    constexpr int MERGE_AHEAD = 4;
+    u32x4 v[MERGE_AHEAD][MERGE_CHUNK];
+    float lv[MERGE_AHEAD][MERGE_CHUNK];
+    const int nch = (S + MERGE_CHUNK - 1) / MERGE_CHUNK;
+#pragma unroll
+    for (int k = 0; k < MERGE_AHEAD; k++)
+      if (k < nch) load(0, k * MERGE_CHUNK, lv[k], v[k]);
+    for (int c = 0; c < nch; c += MERGE_AHEAD) {
+#pragma unroll
+      for (int k = 0; k < MERGE_AHEAD; k++) {
+        if (c + k < nch) {
+          merge_fold8(lv[k], v[k], (c + k) * MERGE_CHUNK, S, mx[0], wsum[0], acc[0]);
+          if (c + k + MERGE_AHEAD < nch)
+            load(0, (c + k + MERGE_AHEAD) * MERGE_CHUNK, lv[k], v[k]);
+        }
+      }
+    }
   } else {
     for (int s0 = 0; s0 < S; s0 += MERGE_CHUNK) {
       u32x4 v[NR][MERGE_CHUNK];
