@@ -1148,21 +1148,59 @@ __global__ __launch_bounds__(64) void merge_splits_f32_kernel(const T* __restric
 
 // bf16 partials: 64 lanes per (b, h) row, 8 latent features (16 bytes) per
 // lane, four rows per workgroup (the per-row arithmetic is merge_rows8).
+// Rows of more than MERGE_SPLIT_PARTS_ABOVE splits: two rows per workgroup,
+// wave (part, row) folds one of the row's two parts and the part-1 state
+// meets part 0 in LDS (the arithmetic of merge_rows8 for such rows, so the
+// same bits, with half the memory round trips per wave).
 __global__ __launch_bounds__(256) void merge_splits_bf16_kernel(const uint16_t* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_lse,
                                                                 int S, int64_t BH,
                                                                 uint16_t* __restrict__ out,
                                                                 float* __restrict__ lse) {
+  __shared__ float xs[2][10][64];  // part-1 states (max, sum, 8 accumulators) of two rows
+  const int lane = threadIdx.x & 63;
+  const int c0 = lane * 8;
+  if (S > MERGE_SPLIT_PARTS_ABOVE) {
+    const int wave = threadIdx.x >> 6;
+    const int part = wave >> 1, r = wave & 1;
+    const int64_t bh = static_cast<int64_t>(blockIdx.x) * 2 + r;
+    const bool ok = bh < BH;
+    float mx = -INFINITY, wsum = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    if (ok)
+      merge_chunks<true>(ws_o, ws_lse, S, BH, bh, c0, merge_part_begin(S, part),
+                         merge_part_end(S, part), mx, wsum, acc);
+    if (part == 1) {
+      xs[r][0][lane] = mx;
+      xs[r][1][lane] = wsum;
+#pragma unroll
+      for (int i = 0; i < 8; i++) xs[r][2 + i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (part == 0 && ok) {
+      float a1[8], o8[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) a1[i] = xs[r][2 + i][lane];
+      merge_combine2(mx, wsum, acc, xs[r][0][lane], xs[r][1][lane], a1);
+      const float l = merge_finish(mx, wsum, acc, o8);
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = pack_bf16x2(o8[2 * i], o8[2 * i + 1]);
+      st16(out + bh * D_C + c0, o);
+      if (lane == 0 && lse) lse[bh] = l;
+    }
+    return;
+  }
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
-  const int c0 = (threadIdx.x & 63) * 8;
   float o8[1][8], l;
   merge_rows8<1, true>(ws_o, ws_lse, S, BH, &bh, c0, o8, &l);
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; i++) o[i] = pack_bf16x2(o8[0][2 * i], o8[0][2 * i + 1]);
   st16(out + bh * D_C + c0, o);
-  if ((threadIdx.x & 63) == 0 && lse) lse[bh] = l;
+  if (lane == 0 && lse) lse[bh] = l;
 }
 
 // ---------------------------------------------------------------------------
@@ -1277,7 +1315,9 @@ hipError_t launch_decode(const DecodeParams& p, bool is_bf16, hipStream_t stream
   if (e != hipSuccess || p.num_splits == 1 || !merge_splits) return e;
   const int64_t BH = static_cast<int64_t>(p.B) * p.n_h;
   if (is_bf16)
-    hipLaunchKernelGGL(merge_splits_bf16_kernel, dim3(static_cast<unsigned>((BH + 3) / 4)),
+    hipLaunchKernelGGL(merge_splits_bf16_kernel,
+                       dim3(static_cast<unsigned>(p.num_splits > MERGE_SPLIT_PARTS_ABOVE
+                                                      ? (BH + 1) / 2 : (BH + 3) / 4)),
                        dim3(256), 0, stream, static_cast<const uint16_t*>(p.ws_o), p.ws_lse,
                        p.num_splits, BH, static_cast<uint16_t*>(p.out_lat), p.lse);
   else

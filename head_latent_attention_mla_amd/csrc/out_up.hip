@@ -145,7 +145,47 @@ __global__ __launch_bounds__(512) void merge_out_up_bf16_kernel(
     for (int k = 0; k < 8 * NQ; k++) bw[k] = ld16(wrow + 16 * k);
   }
   const int64_t BH = static_cast<int64_t>(B) * n_h;
-  {
+  if (S > MERGE_SPLIT_PARTS_ABOVE && B - bt * MO_ROWS <= 4) {
+    // at most 4 rows of many splits: wave (part, r) folds part `part` of row
+    // r, the part-1 states meet part 0 through `red` (free until the quarter
+    // sums); the arithmetic of merge_rows8 for such rows, so the same bits.
+    // Waves 0..3 write merged rows 0..3 of the tile, every other row is zeros.
+    const int part = wave >> 2, r = wave & 3;
+    const int bb = bt * MO_ROWS + r;
+    const bool ok = bb < B;
+    const int64_t bhr = static_cast<int64_t>(bb) * n_h + h;
+    float mx = -INFINITY, wsum = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    if (ok)
+      merge_chunks<true, NV == 2 ? 4 : 2>(ws_o, ws_lse, S, BH, bhr, lane * 8,
+                                          merge_part_begin(S, part), merge_part_end(S, part),
+                                          mx, wsum, acc);
+    float* const xs = reinterpret_cast<float*>(red);  // [4 rows][10][64]
+    if (part == 1) {
+      xs[(r * 10 + 0) * 64 + lane] = mx;
+      xs[(r * 10 + 1) * 64 + lane] = wsum;
+#pragma unroll
+      for (int i = 0; i < 8; i++) xs[(r * 10 + 2 + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    u32x4 o = u32x4{0u, 0u, 0u, 0u};
+    if (part == 0 && ok) {
+      float a1[8], o8[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) a1[i] = xs[(r * 10 + 2 + i) * 64 + lane];
+      merge_combine2(mx, wsum, acc, xs[(r * 10 + 0) * 64 + lane], xs[(r * 10 + 1) * 64 + lane],
+                     a1);
+      const float l = merge_finish(mx, wsum, acc, o8);
+#pragma unroll
+      for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(o8[2 * q], o8[2 * q + 1]);
+      if (lane == 0 && lse) lse[bhr] = l;
+    }
+    // rows `wave` (merged for waves 0..3) and wave + 8 (zeros)
+    *reinterpret_cast<u32x4*>(ol + wave * (D_C * 2) + 16 * (lane ^ wave)) = o;
+    *reinterpret_cast<u32x4*>(ol + (wave + 8) * (D_C * 2) + 16 * (lane ^ (wave + 8))) =
+        u32x4{0u, 0u, 0u, 0u};
+  } else {
     // rows wave and wave + 8 of the tile; rows past B are zeros in LDS (their
     // products are never stored)
     const int r0 = wave, r1 = wave + 8;

@@ -185,6 +185,41 @@ def test_decode_step_fused_merge_matches_the_separate_kernels(B, S_q, n_h, T):
     assert torch.equal(lse1.cpu(), lse3.cpu())
 
 
+@pytest.mark.parametrize("B,n_h,T,splits", [
+    (2, 128, 8000, 0),    # automatic plan: 125 splits of 2 tiles, 2 rows per tile (parts on two waves)
+    (4, 64, 3000, 47),    # 47 splits, 4 rows: parts on two waves
+    (5, 32, 4000, 52),    # 42 splits of 3 tiles, 5 rows: both parts in one wave
+    (20, 16, 2500, 41),   # 40 splits; tile 0: two rows per wave, both parts in one wave;
+                          # tile 1: 4 rows, parts on two waves
+    (3, 128, 1050, 33),   # 33 splits of one tile: just past the two-part bound
+])
+def test_merge_of_many_splits_fused_and_separate(B, n_h, T, splits):
+    # rows of more than 32 splits are merged in two parts, by two waves or by
+    # one; the fused merge + W^UV and the stand-alone merge must give the same
+    # bits, and both must match the oracle
+    print(f"many-split merge: B={B} n_h={n_h} T={T} splits={splits}", flush=True)
+    inp = multi_inputs(B, 1, n_h, T, torch.bfloat16, seed=B * 11 + n_h + T)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    cache = d["cache"]
+    ntiles = -(-T // 32)
+    req = splits or mla.mla_decode_num_splits(B, n_h, T)
+    S = -(-ntiles // -(-ntiles // req))  # no empty split: whole tiles per split
+    assert S > 32
+    one, lse1 = mla.mla_decode_step(d["q_nope"], d["q_pe"], d["wkv_b"], cache[..., :512],
+                                    cache[..., 512:], num_splits=splits, want_lse=True)
+    q_lat = mla.mla_absorb_q(d["q_nope"].reshape(B, n_h, 128), d["wkv_b"])
+    o_lat, lse3 = mla.mla_decode_latent_attn_multi(q_lat.reshape(B, 1, n_h, 512), d["q_pe"],
+                                                   cache[..., :512], cache[..., 512:],
+                                                   num_splits=splits, want_lse=True)
+    three = mla.mla_out_up(o_lat.reshape(B, n_h, 512), d["wkv_b"]).reshape(B, 1, n_h, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu().view(torch.int16), three.cpu().view(torch.int16))
+    assert torch.equal(lse1.cpu(), lse3.cpu())
+    ref, ref_lse = oracle_step(inp, False, None)
+    check(f64(one), ref, TOL[torch.bfloat16], "out")
+    check(f64(lse1), ref_lse, TOL[torch.bfloat16], "lse")
+
+
 def unpack_queries(packed, B, S_q, n_h):
     """Row layout [B, S_q, n_h, 512] of packed queries, by the slot formula
     the header states (plain numpy indexing)."""
