@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--tp", type=int, default=1, metavar="G",
                     help="one GPU's tensor-parallel share of a decode workload: 128/G heads "
                          "(the whole cache is still read)")
+    ap.add_argument("--splits", type=int, default=0, metavar="S",
+                    help="decode workloads: split the attended positions of each sequence into "
+                         "S parts (0: the library's automatic plan)")
     ap.add_argument("--yarn", action="store_true",
                     help="use the context-extended (YaRN) attention scale: "
                          "max_seq_len 163840 > 4096, mscale 1, rope_factor 40")
@@ -511,11 +514,11 @@ def main():
     o_lat = torch.empty((B, n_h, 512), dtype=torch.bfloat16, device=dev)
     out = torch.empty((B, n_h, 128), dtype=torch.bfloat16, device=dev)
     K = rows if sparse else 0
-    ws_bytes = mla.mla_decode_workspace_bytes(B, n_h, T, K, 0)
+    ws_bytes = mla.mla_decode_workspace_bytes(B, n_h, T, K, args.splits)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    splits = mla.mla_decode_num_splits(B, n_h, T, K)
+    splits = args.splits or mla.mla_decode_num_splits(B, n_h, T, K)
 
-    step_ws_bytes = mla.mla_decode_step_workspace_bytes(B, 1, n_h, T, K, 0)
+    step_ws_bytes = mla.mla_decode_step_workspace_bytes(B, 1, n_h, T, K, args.splits)
     step_ws = torch.empty(max(step_ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step(r, ev=None):
@@ -526,13 +529,13 @@ def main():
             mla.mla_absorb_q(x["q_nope"], x["w"], q_lat)
             mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
                                        x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
-                                       out_lat=o_lat, workspace=ws)
+                                       num_splits=args.splits, out_lat=o_lat, workspace=ws)
             mla.mla_out_up(o_lat, x["w"], out)
         else:
             # one call: absorb, split attention, split merge fused into W^UV
             mla.mla_decode_step(x["q_nope"], x["q_pe"], x["w"], x["cache"][..., :512],
                                 x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
-                                out=out, workspace=step_ws)
+                                num_splits=args.splits, out=out, workspace=step_ws)
         if ev is not None:
             ev[1].record()
 
@@ -568,11 +571,12 @@ def main():
         if packed:
             mla.mla_decode_latent_attn_packed(q_lat.view(B, -1), x["q_pe"], x["cache"][..., :512],
                                               x["cache"][..., 512:], topk_idx=x["topk"],
-                                              scale=scale, out_lat=o_lat, workspace=ws)
+                                              scale=scale, num_splits=args.splits,
+                                              out_lat=o_lat, workspace=ws)
         else:
             mla.mla_decode_latent_attn(q_lat, x["q_pe"], x["cache"][..., :512],
                                        x["cache"][..., 512:], topk_idx=x["topk"], scale=scale,
-                                       out_lat=o_lat, workspace=ws)
+                                       num_splits=args.splits, out_lat=o_lat, workspace=ws)
 
     def call_out_up(r):
         x = reps[r]
