@@ -192,6 +192,8 @@ def test_decode_step_fused_merge_matches_the_separate_kernels(B, S_q, n_h, T):
     (20, 16, 2500, 41),   # 40 splits; tile 0: two rows per wave, both parts in one wave;
                           # tile 1: 4 rows, parts on two waves
     (3, 128, 1050, 33),   # 33 splits of one tile: just past the two-part bound
+    (2, 256, 4096, 0),    # 64 splits, 256 (head, tile) workgroups: the one-part-per-quarter
+                          # W^UV layout with the parts on two waves
 ])
 def test_merge_of_many_splits_fused_and_separate(B, n_h, T, splits):
     # rows of more than 32 splits are merged in two parts, by two waves or by
